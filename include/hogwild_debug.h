@@ -1,0 +1,45 @@
+/*
+ * hogwild_debug.h -- host-only introspection of the Hogwild! decode library, for tests.
+ *
+ * These calls touch no GPU and enqueue nothing, so the host logic (slot assignment, page
+ * allocation, view resolution, validation) can be checked bit-exactly on a machine without
+ * a GPU. Same status codes and validation rules as hogwild.h.
+ */
+#ifndef HOGWILD_DEBUG_H
+#define HOGWILD_DEBUG_H
+
+#include "hogwild.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The host half of hw_append_kv without the kernel: validates, takes pages from the free
+ * list and advances the blocks' lengths exactly as hw_append_kv would, WITHOUT writing any
+ * K/V (the pool slots keep whatever they held). Writes the copy plan to runs[cap][5]:
+ * {input row of the first token, page id, first token slot in the page, token count,
+ * local position of the first token}; one run never crosses a page. *n_runs gets the
+ * count even when it exceeds cap (then nothing is mutated and HW_ERR_INVALID_ARG is
+ * returned). Blocks cited by the pages' append step: summary s8, s9. */
+hw_status hw_debug_reserve(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const int32_t *block_ids,
+                           const int32_t *n_tokens, int32_t *runs, int32_t cap, int32_t *n_runs);
+
+/* The view resolution hw_concurrent_decode would upload for `layer` (summary s5 step 3,
+ * s9: each block's start in each worker's view -> the query rotation per (worker, block)).
+ *   segs[cap_segs]                 block id of each segment of the union of the views, in
+ *                                  order of first appearance (worker 0's view first)
+ *   delta[cap_segs][n_workers]     q_pos(w) - offset(w, block), or -1 if w does not see it
+ *   groups[cap_groups][4]          {page, 32-token group within the page, segment, valid
+ *                                  tokens 1..32} of every token group of every segment
+ *   *n_splits                      KV partitions per head a decode would use now
+ * Counts are written even when they exceed the caps (then the arrays are left untouched and
+ * HW_ERR_INVALID_ARG is returned). Validation failures return HW_ERR_STALE_VIEW. */
+hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *delta,
+                           int32_t cap_segs, int32_t *n_segs, int32_t *groups,
+                           int32_t cap_groups, int32_t *n_groups, int32_t *n_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HOGWILD_DEBUG_H */

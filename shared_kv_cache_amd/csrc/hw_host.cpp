@@ -1,0 +1,748 @@
+// Host core of the Hogwild! concurrent-attention decode library: context, page pool,
+// block registry, view resolution and the C ABI (include/hogwild.h, hogwild_debug.h).
+//
+// [Hogwild! Inference paper summary, gentlecold.top]
+//   s5  the concatenation identity and its five steps: each block stored once, local
+//       positions from 0, per-worker block offsets, a query rotation per block, one softmax;
+//   s8  the step: every worker appends its token, then each worker's view is built, then
+//       attention runs with the per-block query rotation;
+//   s9  the cache is a common block plus one current block per worker, each holding every
+//       layer's K/V at local positions; the view is computed at attention time; the kernel
+//       balances work by KV entries and reduces partial results.
+// [ocdem.com article on Hogwild! Inference] s2.1 neighbour blocks in ascending worker ID
+//   (the caller's view lists carry that order); s3.1 page-table metadata (owner, paragraph)
+//   is the caller's: this library keys blocks by caller-chosen ids only.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "hogwild.h"
+#include "hogwild_debug.h"
+#include "hw_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kStagingSlots = 4;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct BlockState {
+  std::vector<int32_t> pages;  // page ids in block order (shared by all layers)
+  std::vector<int32_t> len;    // tokens per layer
+  int32_t max_len() const {
+    int32_t m = 0;
+    for (int32_t x : len) m = std::max(m, x);
+    return m;
+  }
+};
+
+struct Views {
+  bool set = false;
+  int32_t n_workers = 0;
+  std::vector<std::vector<int32_t>> blocks;
+  std::vector<std::vector<int64_t>> offsets;  // empty inner vectors: running sum
+  bool has_offsets = false;
+  std::vector<int64_t> q_pos;
+  bool has_qpos = false;
+  uint64_t version = 0;
+};
+
+// What one decode uploads: per-(segment, worker) query offsets and the token-group list.
+struct Resolution {
+  std::vector<int32_t> seg_blocks;
+  std::vector<int32_t> delta;   // [n_seg][n_workers]
+  std::vector<int32_t> g_page, g_gip, g_seg, g_valid;
+  int32_t n_workers = 0;
+};
+
+}  // namespace
+
+struct hw_ctx {
+  hw_config cfg{};
+  std::vector<BlockState> blocks;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  uint64_t page_generation = 0;     // bumped whenever a page leaves a block
+  Views views;
+  std::string err;
+  int32_t split_override = 0;
+  int32_t num_cus = 256;
+
+  // device workspace carve-up
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  size_t off_trig = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0, tables_bytes = 0;
+  size_t part_o_bytes = 0, part_lse_bytes = 0, total_bytes = 0;
+
+  // upload cache
+  std::vector<int64_t> uploaded_sig;
+  bool uploaded_valid = false;
+  int32_t up_n_groups = 0, up_n_seg = 0, up_n_workers = 0;
+  size_t up_groups_off = 0;  // byte offset of the group list inside the tables region
+
+  // pinned staging ring
+  char *staging = nullptr;
+  hipEvent_t events[kStagingSlots] = {};
+  bool event_live[kStagingSlots] = {};
+  int next_slot = 0;
+  bool debug_sync = false;
+
+  hw_status fail(hw_status s, const std::string &m) {
+    err = m;
+    return s;
+  }
+};
+
+namespace {
+
+thread_local std::string g_create_error;
+
+uint64_t splitmix64_next(uint64_t &state) {
+  uint64_t z = (state += 0x9E3779B97F4A7C15ULL);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+int32_t rows_total(const hw_ctx *c, int32_t n_workers) {
+  return n_workers * (c->cfg.n_q_heads / c->cfg.n_kv_heads);
+}
+
+void layout_workspace(hw_ctx *c) {
+  const hw_config &g = c->cfg;
+  const size_t half = (size_t)g.head_dim / 2;
+  const size_t max_groups = (size_t)g.n_pages * (g.page_size / hw::kTokGroup);
+  const size_t max_rows = (size_t)g.max_workers * (g.n_q_heads / g.n_kv_heads);
+  size_t off = 0;
+  c->off_trig = off;
+  off = align_up(off + (size_t)g.max_position * half * 2 * sizeof(float));
+  c->off_tables = off;
+  c->tables_bytes = align_up((size_t)g.max_blocks * g.max_workers * sizeof(int32_t)) +
+                    align_up(max_groups * 2 * sizeof(int32_t));
+  off = align_up(off + c->tables_bytes);
+  c->off_part_o = off;
+  c->part_o_bytes = (size_t)g.max_splits * g.n_kv_heads * max_rows * g.head_dim * sizeof(float);
+  off = align_up(off + c->part_o_bytes);
+  c->off_part_lse = off;
+  c->part_lse_bytes = (size_t)g.max_splits * g.n_kv_heads * max_rows * sizeof(float);
+  off = align_up(off + c->part_lse_bytes);
+  c->total_bytes = off;
+}
+
+hw_status check_config(const hw_config *g, std::string &m) {
+  if (!g) return m = "cfg is NULL", HW_ERR_INVALID_ARG;
+  if (g->n_layers <= 0) return m = "n_layers must be > 0", HW_ERR_INVALID_ARG;
+  if (g->n_kv_heads <= 0 || g->n_q_heads <= 0 || g->n_q_heads % g->n_kv_heads)
+    return m = "n_q_heads must be a positive multiple of n_kv_heads", HW_ERR_INVALID_ARG;
+  if (g->head_dim != 64 && g->head_dim != 128) return m = "head_dim must be 64 or 128", HW_ERR_INVALID_ARG;
+  if (g->page_size <= 0 || g->page_size % hw::kTokGroup || g->page_size > 8192)
+    return m = "page_size must be a multiple of 32 in [32, 8192]", HW_ERR_INVALID_ARG;
+  if (g->n_pages <= 0) return m = "n_pages must be > 0", HW_ERR_INVALID_ARG;
+  if (g->max_blocks <= 0 || g->max_blocks > (1 << 22)) return m = "max_blocks out of range", HW_ERR_INVALID_ARG;
+  if (g->max_workers <= 0 || g->max_workers > 1024) return m = "max_workers out of range", HW_ERR_INVALID_ARG;
+  if (g->max_position <= 0) return m = "max_position must be > 0", HW_ERR_INVALID_ARG;
+  if (g->max_splits < 0 || g->max_splits > 65535) return m = "max_splits out of range", HW_ERR_INVALID_ARG;
+  if (g->kv_dtype != HW_BF16 && g->kv_dtype != HW_F32) return m = "unknown kv_dtype", HW_ERR_INVALID_ARG;
+  if (!(g->rope_theta > 1.0) || !std::isfinite(g->rope_theta)) return m = "rope_theta must be > 1", HW_ERR_INVALID_ARG;
+  if (!(g->softmax_scale >= 0.0f) || !std::isfinite(g->softmax_scale))
+    return m = "softmax_scale must be finite and >= 0", HW_ERR_INVALID_ARG;
+  if (!g->k_pool || !g->v_pool) return m = "k_pool and v_pool must be set", HW_ERR_INVALID_ARG;
+  if (((uintptr_t)g->k_pool | (uintptr_t)g->v_pool) % kAlign) return m = "pools must be 256-byte aligned", HW_ERR_INVALID_ARG;
+  const double elems = (double)g->n_layers * g->n_pages * g->n_kv_heads * g->page_size * g->head_dim;
+  if (elems > 9.0e18 / 4) return m = "pool too large", HW_ERR_INVALID_ARG;
+  return HW_OK;
+}
+
+size_t kv_elem_bytes(const hw_ctx *c) { return c->cfg.kv_dtype == HW_BF16 ? 2 : 4; }
+
+size_t layer_elems(const hw_ctx *c) {
+  const hw_config &g = c->cfg;
+  return (size_t)g.n_pages * g.n_kv_heads * g.page_size * g.head_dim;
+}
+
+// ---- append planning -------------------------------------------------------------
+
+struct AppendPlan {
+  std::vector<hw::AppendRun> runs;
+  std::vector<int32_t> new_pages_per_block;  // per call entry
+  int32_t total_new_pages = 0;
+};
+
+hw_status plan_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *ids,
+                      const int32_t *n_tokens, AppendPlan &plan) {
+  const hw_config &g = c->cfg;
+  if (layer < 0 || layer >= g.n_layers) return c->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (n_blocks < 0) return c->fail(HW_ERR_INVALID_ARG, "n_blocks < 0");
+  if (n_blocks > 0 && (!ids || !n_tokens)) return c->fail(HW_ERR_INVALID_ARG, "block_ids/n_tokens NULL");
+  std::vector<char> seen(g.max_blocks, 0);
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const int32_t b = ids[i];
+    if (b < 0 || b >= g.max_blocks) return c->fail(HW_ERR_INVALID_ARG, "block id out of range");
+    if (seen[b]) return c->fail(HW_ERR_INVALID_ARG, "block id repeated in one append");
+    seen[b] = 1;
+    if (n_tokens[i] < 0) return c->fail(HW_ERR_INVALID_ARG, "n_tokens < 0");
+    const int64_t end = (int64_t)c->blocks[b].len[layer] + n_tokens[i];
+    if (end > g.max_position) return c->fail(HW_ERR_INVALID_ARG, "local position would reach max_position");
+    if (end > (int64_t)g.n_pages * g.page_size) return c->fail(HW_ERR_OUT_OF_PAGES, "block longer than the pool");
+  }
+  plan.runs.clear();
+  plan.new_pages_per_block.assign(n_blocks, 0);
+  plan.total_new_pages = 0;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const BlockState &bs = c->blocks[ids[i]];
+    const int32_t new_len = bs.len[layer] + n_tokens[i];
+    const int32_t need = (std::max(bs.max_len(), new_len) + g.page_size - 1) / g.page_size;
+    const int32_t add = std::max<int32_t>(0, need - (int32_t)bs.pages.size());
+    plan.new_pages_per_block[i] = add;
+    plan.total_new_pages += add;
+  }
+  if ((size_t)plan.total_new_pages > c->free_stack.size())
+    return c->fail(HW_ERR_OUT_OF_PAGES, "not enough free pages: need " +
+                                            std::to_string(plan.total_new_pages) + ", have " +
+                                            std::to_string(c->free_stack.size()));
+  // Pages come off the back of the free stack in call order.
+  size_t taken = 0;
+  int32_t row = 0;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const BlockState &bs = c->blocks[ids[i]];
+    std::vector<int32_t> pages = bs.pages;
+    for (int32_t k = 0; k < plan.new_pages_per_block[i]; ++k)
+      pages.push_back(c->free_stack[c->free_stack.size() - 1 - taken++]);
+    int32_t pos = bs.len[layer], left = n_tokens[i];
+    while (left > 0) {
+      const int32_t slot = pos % g.page_size;
+      const int32_t cnt = std::min(left, g.page_size - slot);
+      plan.runs.push_back(hw::AppendRun{row, pages[pos / g.page_size], slot, cnt, pos});
+      row += cnt;
+      pos += cnt;
+      left -= cnt;
+    }
+  }
+  return HW_OK;
+}
+
+void commit_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *ids,
+                   const int32_t *n_tokens, const AppendPlan &plan) {
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    BlockState &bs = c->blocks[ids[i]];
+    for (int32_t k = 0; k < plan.new_pages_per_block[i]; ++k) {
+      bs.pages.push_back(c->free_stack.back());
+      c->free_stack.pop_back();
+    }
+    bs.len[layer] += n_tokens[i];
+  }
+}
+
+// ---- view resolution ---------------------------------------------------------------
+
+int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
+  const int32_t row_blocks = (rows_total(c, n_workers) + hw::kRowsPerBlock - 1) / hw::kRowsPerBlock;
+  const int32_t per_head = c->cfg.n_kv_heads * std::max(1, row_blocks);
+  int32_t s = (c->num_cus + per_head - 1) / per_head;
+  s = std::min(s, std::max(1, n_groups / 8));
+  return std::max(1, std::min(s, c->cfg.max_splits));
+}
+
+int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
+  if (c->split_override > 0) return std::min(c->split_override, c->cfg.max_splits);
+  return auto_splits(c, n_groups, n_workers);
+}
+
+// Signature of everything a resolution depends on; equal signatures => equal tables.
+std::vector<int64_t> signature(const hw_ctx *c, int32_t layer) {
+  std::vector<int64_t> s;
+  s.push_back((int64_t)c->views.version);
+  s.push_back((int64_t)c->page_generation);
+  for (const auto &v : c->views.blocks)
+    for (int32_t b : v) {
+      s.push_back(c->blocks[b].len[layer]);
+      s.push_back((int64_t)c->blocks[b].pages.size());
+    }
+  return s;
+}
+
+hw_status resolve(hw_ctx *c, int32_t layer, Resolution &r) {
+  const hw_config &g = c->cfg;
+  const Views &v = c->views;
+  if (!v.set) return c->fail(HW_ERR_STALE_VIEW, "no views set");
+  const int32_t n = v.n_workers;
+  r = Resolution();
+  r.n_workers = n;
+  std::vector<int32_t> seg_of(g.max_blocks, -1);
+  std::vector<std::vector<int64_t>> offs(n);
+  std::vector<int64_t> qpos(n);
+  for (int32_t w = 0; w < n; ++w) {
+    const auto &vb = v.blocks[w];
+    auto &o = offs[w];
+    if (v.has_offsets) {
+      o = v.offsets[w];
+    } else {
+      int64_t acc = 0;
+      for (int32_t b : vb) {
+        o.push_back(acc);
+        acc += c->blocks[b].len[layer];
+      }
+    }
+    if (v.has_qpos) {
+      qpos[w] = v.q_pos[w];
+    } else {
+      qpos[w] = vb.empty() ? -1 : o.back() + c->blocks[vb.back()].len[layer] - 1;
+    }
+    // overlaps and causality, over the blocks that hold tokens in this layer
+    std::vector<std::pair<int64_t, int64_t>> spans;
+    for (size_t i = 0; i < vb.size(); ++i) {
+      const int64_t len = c->blocks[vb[i]].len[layer];
+      if (len == 0) continue;
+      spans.emplace_back(o[i], o[i] + len);
+      if (o[i] + len - 1 > qpos[w])
+        return c->fail(HW_ERR_STALE_VIEW, "worker " + std::to_string(w) + ": block " +
+                                              std::to_string(vb[i]) + " has a key after q_pos");
+      if (qpos[w] - o[i] >= g.max_position)
+        return c->fail(HW_ERR_STALE_VIEW, "worker " + std::to_string(w) +
+                                              ": query offset reaches max_position");
+    }
+    std::sort(spans.begin(), spans.end());
+    for (size_t i = 1; i < spans.size(); ++i)
+      if (spans[i].first < spans[i - 1].second)
+        return c->fail(HW_ERR_STALE_VIEW, "worker " + std::to_string(w) + ": overlapping blocks");
+    for (int32_t b : vb)
+      if (c->blocks[b].len[layer] > 0 && seg_of[b] < 0) {
+        seg_of[b] = (int32_t)r.seg_blocks.size();
+        r.seg_blocks.push_back(b);
+      }
+  }
+  const int32_t n_seg = (int32_t)r.seg_blocks.size();
+  r.delta.assign((size_t)n_seg * n, -1);
+  for (int32_t w = 0; w < n; ++w) {
+    const auto &vb = v.blocks[w];
+    for (size_t i = 0; i < vb.size(); ++i) {
+      const int32_t s = seg_of[vb[i]];
+      if (s >= 0) r.delta[(size_t)s * n + w] = (int32_t)(qpos[w] - offs[w][i]);
+    }
+  }
+  const int32_t gpp = g.page_size / hw::kTokGroup;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const BlockState &bs = c->blocks[r.seg_blocks[s]];
+    const int32_t len = bs.len[layer];
+    for (int32_t t = 0; t < len; t += hw::kTokGroup) {
+      r.g_page.push_back(bs.pages[t / g.page_size]);
+      r.g_gip.push_back((t % g.page_size) / hw::kTokGroup);
+      r.g_seg.push_back(s);
+      r.g_valid.push_back(std::min(hw::kTokGroup, len - t));
+    }
+  }
+  (void)gpp;
+  return HW_OK;
+}
+
+// ---- device helpers ----------------------------------------------------------------
+
+hw_status hip_fail(hw_ctx *c, hipError_t e, const char *what) {
+  return c->fail(HW_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hw_status ensure_staging(hw_ctx *c) {
+  if (c->staging) return HW_OK;
+  hipError_t e = hipHostMalloc((void **)&c->staging, c->tables_bytes * kStagingSlots, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    c->staging = nullptr;
+    return hip_fail(c, e, "hipHostMalloc(staging)");
+  }
+  for (int i = 0; i < kStagingSlots; ++i) {
+    e = hipEventCreateWithFlags(&c->events[i], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventCreate");
+  }
+  return HW_OK;
+}
+
+hw_status post_launch(hw_ctx *c, hipError_t e, const char *what, hipStream_t s) {
+  if (e != hipSuccess) return hip_fail(c, e, what);
+  if (c->debug_sync) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(c, e, what);
+  }
+  return HW_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+// C ABI
+// =====================================================================================
+
+extern "C" {
+
+hw_status hw_create(const hw_config *cfg, hw_ctx **out) {
+  if (!out) {
+    g_create_error = "out is NULL";
+    return HW_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  std::string m;
+  hw_status st = check_config(cfg, m);
+  if (st != HW_OK) {
+    g_create_error = m;
+    return st;
+  }
+  hw_ctx *c = new (std::nothrow) hw_ctx();
+  if (!c) {
+    g_create_error = "out of host memory";
+    return HW_ERR_INVALID_ARG;
+  }
+  c->cfg = *cfg;
+  if (c->cfg.max_splits == 0) c->cfg.max_splits = 256;
+  if (c->cfg.softmax_scale == 0.0f) c->cfg.softmax_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
+  c->blocks.resize(cfg->max_blocks);
+  for (auto &b : c->blocks) b.len.assign(cfg->n_layers, 0);
+  std::vector<int32_t> order(cfg->n_pages);
+  for (int32_t i = 0; i < cfg->n_pages; ++i) order[i] = i;
+  if (cfg->page_seed != 0) {
+    uint64_t state = cfg->page_seed;
+    for (int32_t i = cfg->n_pages - 1; i >= 1; --i) {
+      const int32_t j = (int32_t)(splitmix64_next(state) % (uint64_t)(i + 1));
+      std::swap(order[i], order[j]);
+    }
+  }
+  c->free_stack.assign(order.rbegin(), order.rend());
+  const char *dbg = std::getenv("HW_DEBUG_SYNC");
+  c->debug_sync = dbg && dbg[0] == '1';
+  layout_workspace(c);
+  *out = c;
+  return HW_OK;
+}
+
+hw_status hw_destroy(hw_ctx *ctx) {
+  if (!ctx) return HW_OK;
+  for (int i = 0; i < kStagingSlots; ++i)
+    if (ctx->events[i]) (void)hipEventDestroy(ctx->events[i]);
+  if (ctx->staging) (void)hipHostFree(ctx->staging);
+  delete ctx;
+  return HW_OK;
+}
+
+const char *hw_last_error(const hw_ctx *ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+size_t hw_workspace_bytes(const hw_ctx *ctx) { return ctx ? ctx->total_bytes : 0; }
+
+hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (!dev) return ctx->fail(HW_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)dev % kAlign) return ctx->fail(HW_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < ctx->total_bytes)
+    return ctx->fail(HW_ERR_WORKSPACE, "workspace too small: need " + std::to_string(ctx->total_bytes));
+  const hw_config &g = ctx->cfg;
+  // cos/sin of p * theta^(-2j/d), p < max_position: fp64 libm, rounded once to fp32.
+  const int half = g.head_dim / 2;
+  std::vector<double> inv(half);
+  for (int j = 0; j < half; ++j) inv[j] = std::pow(g.rope_theta, -(2.0 * j) / (double)g.head_dim);
+  std::vector<float> table((size_t)g.max_position * half * 2);
+  const unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::vector<std::thread> pool;
+  for (unsigned t = 0; t < nthreads; ++t)
+    pool.emplace_back([&, t]() {
+      for (int64_t p = t; p < g.max_position; p += nthreads)
+        for (int j = 0; j < half; ++j) {
+          const double a = (double)p * inv[j];
+          table[((size_t)p * half + j) * 2] = (float)std::cos(a);
+          table[((size_t)p * half + j) * 2 + 1] = (float)std::sin(a);
+        }
+    });
+  for (auto &th : pool) th.join();
+  hipError_t e = hipMemcpy((char *)dev + ctx->off_trig, table.data(), table.size() * sizeof(float),
+                           hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(rope table)");
+  int dev_id = 0;
+  if (hipGetDevice(&dev_id) == hipSuccess) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id) == hipSuccess && cus > 0)
+      ctx->num_cus = cus;
+  }
+  ctx->ws = dev;
+  ctx->ws_bytes = bytes;
+  ctx->uploaded_valid = false;
+  return HW_OK;
+}
+
+hw_status hw_append_kv(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const int32_t *block_ids,
+                       const int32_t *n_tokens, const void *k, const void *v, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  AppendPlan plan;
+  hw_status st = plan_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
+  if (st != HW_OK) return st;
+  if (plan.runs.empty()) return HW_OK;
+  if (!k || !v) return ctx->fail(HW_ERR_INVALID_ARG, "k/v NULL");
+  // Save what commit changes so a failed launch can be rolled back.
+  const std::vector<int32_t> saved_free = ctx->free_stack;
+  std::vector<BlockState> saved;
+  for (int32_t i = 0; i < n_blocks; ++i) saved.push_back(ctx->blocks[block_ids[i]]);
+  commit_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
+
+  const hw_config &g = ctx->cfg;
+  const size_t eb = kv_elem_bytes(ctx);
+  hw::AppendArgs a{};
+  a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.v_layer = (char *)g.v_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.k_src = k;
+  a.v_src = v;
+  a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
+  a.n_kv_heads = g.n_kv_heads;
+  a.page_groups = g.page_size / hw::kTokGroup;
+  hipStream_t s = (hipStream_t)stream;
+  for (size_t r0 = 0; r0 < plan.runs.size(); r0 += hw::kMaxRunsPerLaunch) {
+    const size_t n = std::min(plan.runs.size() - r0, (size_t)hw::kMaxRunsPerLaunch);
+    a.n_runs = (int32_t)n;
+    std::memcpy(a.runs, plan.runs.data() + r0, n * sizeof(hw::AppendRun));
+    hw_status ls = post_launch(ctx, hw::launch_append(g.kv_dtype, g.head_dim, a, s), "rope_append", s);
+    if (ls != HW_OK) {
+      ctx->free_stack = saved_free;
+      for (int32_t i = 0; i < n_blocks; ++i) ctx->blocks[block_ids[i]] = saved[i];
+      return ls;
+    }
+  }
+  return HW_OK;
+}
+
+hw_status hw_set_views(hw_ctx *ctx, int32_t n_workers, const int32_t *view_len,
+                       const int32_t *view_blocks, const int64_t *view_offsets,
+                       const int64_t *q_pos) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  if (n_workers <= 0 || n_workers > g.max_workers)
+    return ctx->fail(HW_ERR_INVALID_ARG, "n_workers must be in [1, max_workers]");
+  if (!view_len) return ctx->fail(HW_ERR_INVALID_ARG, "view_len NULL");
+  int64_t total = 0;
+  for (int32_t w = 0; w < n_workers; ++w) {
+    if (view_len[w] < 0 || view_len[w] > g.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "view_len out of range");
+    total += view_len[w];
+  }
+  if (total > 0 && !view_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "view_blocks NULL");
+  Views nv;
+  nv.set = true;
+  nv.n_workers = n_workers;
+  nv.has_offsets = view_offsets != nullptr;
+  nv.has_qpos = q_pos != nullptr;
+  std::vector<char> seen(g.max_blocks, 0);
+  int64_t k = 0;
+  for (int32_t w = 0; w < n_workers; ++w) {
+    std::vector<int32_t> vb(view_blocks + k, view_blocks + k + view_len[w]);
+    std::vector<int64_t> vo;
+    if (view_offsets) vo.assign(view_offsets + k, view_offsets + k + view_len[w]);
+    k += view_len[w];
+    for (int32_t b : vb)
+      if (b < 0 || b >= g.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "view block id out of range");
+    for (int32_t b : vb) {
+      if (seen[b]) {
+        for (int32_t x : vb) seen[x] = 0;
+        return ctx->fail(HW_ERR_INVALID_ARG, "block repeated in a view");
+      }
+      seen[b] = 1;
+    }
+    for (int32_t b : vb) seen[b] = 0;
+    for (int64_t o : vo)
+      if (o < 0 || o >= (int64_t)1 << 40) return ctx->fail(HW_ERR_INVALID_ARG, "view offset out of range");
+    if (q_pos && (q_pos[w] < -1 || q_pos[w] >= (int64_t)1 << 40))
+      return ctx->fail(HW_ERR_INVALID_ARG, "q_pos out of range");
+    nv.blocks.push_back(std::move(vb));
+    nv.offsets.push_back(std::move(vo));
+    if (q_pos) nv.q_pos.push_back(q_pos[w]);
+  }
+  nv.version = ctx->views.version + 1;
+  ctx->views = std::move(nv);
+  return HW_OK;
+}
+
+hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float *out, float *lse,
+                               void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (!q || !out) return ctx->fail(HW_ERR_INVALID_ARG, "q/out NULL");
+  if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  if (!ctx->views.set) return ctx->fail(HW_ERR_STALE_VIEW, "no views set");
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t n = ctx->views.n_workers;
+  char *tables = (char *)ctx->ws + ctx->off_tables;
+
+  std::vector<int64_t> sig = signature(ctx, layer);
+  if (!ctx->uploaded_valid || sig != ctx->uploaded_sig) {
+    Resolution r;
+    hw_status st = resolve(ctx, layer, r);
+    if (st != HW_OK) return st;
+    st = ensure_staging(ctx);
+    if (st != HW_OK) return st;
+    const int32_t n_seg = (int32_t)r.seg_blocks.size();
+    const int32_t n_groups = (int32_t)r.g_page.size();
+    const size_t delta_bytes = align_up((size_t)n_seg * n * sizeof(int32_t));
+    const size_t bytes = delta_bytes + (size_t)n_groups * 2 * sizeof(int32_t);
+    const int slot = ctx->next_slot;
+    ctx->next_slot = (ctx->next_slot + 1) % kStagingSlots;
+    if (ctx->event_live[slot]) {
+      hipError_t e = hipEventSynchronize(ctx->events[slot]);
+      if (e != hipSuccess) return hip_fail(ctx, e, "hipEventSynchronize(staging)");
+    }
+    char *stg = ctx->staging + (size_t)slot * ctx->tables_bytes;
+    if (n_seg) std::memcpy(stg, r.delta.data(), (size_t)n_seg * n * sizeof(int32_t));
+    int32_t *gd = reinterpret_cast<int32_t *>(stg + delta_bytes);
+    const int32_t gpp = g.page_size / hw::kTokGroup;
+    for (int32_t i = 0; i < n_groups; ++i) {
+      gd[2 * i] = r.g_page[i] * g.n_kv_heads * gpp + r.g_gip[i];
+      gd[2 * i + 1] = (r.g_seg[i] << 8) | r.g_valid[i];
+    }
+    if (bytes) {
+      hipError_t e = hipMemcpyAsync(tables, stg, bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpyAsync(view tables)");
+      e = hipEventRecord(ctx->events[slot], s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord(staging)");
+      ctx->event_live[slot] = true;
+    }
+    ctx->uploaded_sig = std::move(sig);
+    ctx->uploaded_valid = true;
+    ctx->up_n_groups = n_groups;
+    ctx->up_n_seg = n_seg;
+    ctx->up_n_workers = n;
+    ctx->up_groups_off = delta_bytes;
+  }
+
+  const int32_t group = g.n_q_heads / g.n_kv_heads;
+  const int32_t rows = n * group;
+  const int32_t n_groups = ctx->up_n_groups;
+  const int32_t splits = choose_splits(ctx, n_groups, n);
+  const size_t eb = kv_elem_bytes(ctx);
+  hw::DecodeArgs a{};
+  a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.v_layer = (char *)g.v_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.groups = reinterpret_cast<const int2 *>(tables + ctx->up_groups_off);
+  a.delta = reinterpret_cast<const int32_t *>(tables);
+  a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
+  a.part_o = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_o);
+  a.part_lse = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_lse);
+  a.n_groups = n_groups;
+  a.n_workers = n;
+  a.n_q_heads = g.n_q_heads;
+  a.n_kv_heads = g.n_kv_heads;
+  a.group = group;
+  a.rows = rows;
+  a.n_splits = splits;
+  a.page_groups = g.page_size / hw::kTokGroup;
+  a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
+  const int32_t row_blocks = (rows + hw::kRowsPerBlock - 1) / hw::kRowsPerBlock;
+  hw_status st = post_launch(ctx, hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s),
+                             "concurrent_decode", s);
+  if (st != HW_OK) return st;
+  if (splits > 1) {
+    hw::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.n_workers = n;
+    m.n_q_heads = g.n_q_heads;
+    m.n_kv_heads = g.n_kv_heads;
+    m.group = group;
+    m.rows = rows;
+    m.n_splits = splits;
+    st = post_launch(ctx, hw::launch_merge(g.head_dim, m, s), "lse_merge", s);
+    if (st != HW_OK) return st;
+  }
+  return HW_OK;
+}
+
+hw_status hw_reset_block(hw_ctx *ctx, int32_t block_id) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (block_id < 0 || block_id >= ctx->cfg.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "block id out of range");
+  BlockState &bs = ctx->blocks[block_id];
+  for (auto it = bs.pages.rbegin(); it != bs.pages.rend(); ++it) ctx->free_stack.push_back(*it);
+  if (!bs.pages.empty()) ctx->page_generation++;
+  bs.pages.clear();
+  std::fill(bs.len.begin(), bs.len.end(), 0);
+  return HW_OK;
+}
+
+hw_status hw_set_split(hw_ctx *ctx, int32_t n_splits) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (n_splits < 0 || n_splits > ctx->cfg.max_splits)
+    return ctx->fail(HW_ERR_INVALID_ARG, "n_splits must be in [0, max_splits]");
+  ctx->split_override = n_splits;
+  return HW_OK;
+}
+
+hw_status hw_block_info(const hw_ctx *ctx, int32_t block_id, int32_t layer, int32_t *length,
+                        int32_t *pages, int32_t cap, int32_t *n_out) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  hw_ctx *c = const_cast<hw_ctx *>(ctx);
+  if (block_id < 0 || block_id >= ctx->cfg.max_blocks) return c->fail(HW_ERR_INVALID_ARG, "block id out of range");
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return c->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  const BlockState &bs = ctx->blocks[block_id];
+  if (length) *length = bs.len[layer];
+  if (n_out) *n_out = (int32_t)bs.pages.size();
+  if (pages)
+    for (int32_t i = 0; i < std::min<int32_t>(cap, (int32_t)bs.pages.size()); ++i) pages[i] = bs.pages[i];
+  return HW_OK;
+}
+
+hw_status hw_free_pages(const hw_ctx *ctx, int32_t *n_free) {
+  if (!ctx || !n_free) return HW_ERR_INVALID_ARG;
+  *n_free = (int32_t)ctx->free_stack.size();
+  return HW_OK;
+}
+
+// ---- hogwild_debug.h ---------------------------------------------------------------
+
+hw_status hw_debug_reserve(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const int32_t *block_ids,
+                           const int32_t *n_tokens, int32_t *runs, int32_t cap, int32_t *n_runs) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  AppendPlan plan;
+  hw_status st = plan_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
+  if (st != HW_OK) return st;
+  if (n_runs) *n_runs = (int32_t)plan.runs.size();
+  if ((int32_t)plan.runs.size() > cap || (!runs && !plan.runs.empty()))
+    return ctx->fail(HW_ERR_INVALID_ARG, "runs buffer too small");
+  for (size_t i = 0; i < plan.runs.size(); ++i) {
+    const hw::AppendRun &r = plan.runs[i];
+    runs[5 * i] = r.src_row;
+    runs[5 * i + 1] = r.page;
+    runs[5 * i + 2] = r.slot0;
+    runs[5 * i + 3] = r.count;
+    runs[5 * i + 4] = r.pos0;
+  }
+  commit_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
+  return HW_OK;
+}
+
+hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *delta,
+                           int32_t cap_segs, int32_t *n_segs, int32_t *groups,
+                           int32_t cap_groups, int32_t *n_groups, int32_t *n_splits) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  Resolution r;
+  hw_status st = resolve(ctx, layer, r);
+  if (st != HW_OK) return st;
+  const int32_t ns = (int32_t)r.seg_blocks.size(), ng = (int32_t)r.g_page.size();
+  if (n_segs) *n_segs = ns;
+  if (n_groups) *n_groups = ng;
+  if (n_splits) *n_splits = choose_splits(ctx, ng, r.n_workers);
+  if (ns > cap_segs || ng > cap_groups) return ctx->fail(HW_ERR_INVALID_ARG, "buffers too small");
+  if (segs) std::copy(r.seg_blocks.begin(), r.seg_blocks.end(), segs);
+  if (delta) std::copy(r.delta.begin(), r.delta.end(), delta);
+  if (groups)
+    for (int32_t i = 0; i < ng; ++i) {
+      groups[4 * i] = r.g_page[i];
+      groups[4 * i + 1] = r.g_gip[i];
+      groups[4 * i + 2] = r.g_seg[i];
+      groups[4 * i + 3] = r.g_valid[i];
+    }
+  return HW_OK;
+}
+
+}  // extern "C"

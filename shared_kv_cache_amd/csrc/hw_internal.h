@@ -1,0 +1,78 @@
+// Internal interface between the host core (hw_host.cpp) and the gfx950 kernels
+// (hw_kernels.hip). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hogwild.h"
+
+namespace hw {
+
+constexpr int kTokGroup = 32;          // tokens per pool group (one MFMA K/V tile)
+constexpr int kWaves = 4;              // waves per decode workgroup
+constexpr int kRowsPerBlock = 64;      // stacked (worker, query head) rows per decode workgroup
+constexpr int kMaxRunsPerLaunch = 64;  // append runs carried in one launch's arguments
+
+// One run of appended tokens: consecutive tokens of one block inside one page.
+struct AppendRun {
+  int32_t src_row;  // row of the first token in the caller's k/v input
+  int32_t page;     // pool page
+  int32_t slot0;    // first token slot within the page
+  int32_t count;    // tokens
+  int32_t pos0;     // block-local position of the first token
+};
+
+struct AppendArgs {
+  void *k_layer;          // pool base of the layer
+  void *v_layer;
+  const void *k_src;      // [rows][n_kv_heads][head_dim]
+  const void *v_src;
+  const float2 *trig;     // [max_position][head_dim/2] (cos, sin)
+  int32_t n_kv_heads;
+  int32_t page_groups;    // page_size / 32
+  int32_t n_runs;
+  AppendRun runs[kMaxRunsPerLaunch];
+};
+
+struct DecodeArgs {
+  const void *k_layer;
+  const void *v_layer;
+  const float *q;          // [n_workers][n_q_heads][head_dim]
+  float *out;              // [n_workers][n_q_heads][head_dim]   (written when n_splits == 1)
+  float *lse;              // [n_workers][n_q_heads] or null      (idem)
+  const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens}
+  const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
+  const float2 *trig;      // [max_position][head_dim/2]
+  float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
+  float *part_lse;         // [n_splits][n_kv_heads][rows] log2-domain partial normalisers
+  int32_t n_groups;
+  int32_t n_workers;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;           // n_q_heads / n_kv_heads
+  int32_t rows;            // n_workers * group
+  int32_t n_splits;
+  int32_t page_groups;
+  float q_scale;           // softmax_scale * log2(e)
+};
+
+struct MergeArgs {
+  const float *part_o;
+  const float *part_lse;
+  float *out;
+  float *lse;
+  int32_t n_workers;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;
+  int32_t rows;
+  int32_t n_splits;
+};
+
+hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStream_t s);
+hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
+                         hipStream_t s);
+hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
+
+}  // namespace hw

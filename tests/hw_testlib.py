@@ -1,0 +1,86 @@
+"""Helpers shared by the GPU tests: fill a cache from a workload, run the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import hogwild_oracle as O
+from shared_kv_cache_amd import hogwild as H
+from shared_kv_cache_amd import workloads as W
+
+DEV = "cuda"
+
+
+def kv_tensor(x: np.ndarray, kv_dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device=DEV, dtype=torch.bfloat16 if kv_dtype == "bf16" else torch.float32)
+
+
+def make_cache(wl: W.Workload, n_layers=None, page_seed=None, max_splits=0, n_pages=None,
+               max_blocks=None, max_position=None, max_workers=None) -> H.HogwildCache:
+    return H.HogwildCache(
+        n_layers=wl.n_layers if n_layers is None else n_layers,
+        n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+        page_size=wl.page_size, n_pages=wl.n_pages if n_pages is None else n_pages,
+        max_blocks=len(wl.blocks()) + 4 if max_blocks is None else max_blocks,
+        max_workers=wl.n_workers if max_workers is None else max_workers,
+        max_position=wl.max_position if max_position is None else max_position,
+        kv_dtype=wl.kv_dtype, page_seed=wl.page_seed if page_seed is None else page_seed,
+        rope_theta=wl.theta, max_splits=max_splits)
+
+
+def fill_layer(cache: H.HogwildCache, wl: W.Workload, layer: int, blocks=None):
+    """Append every block of the workload (step-0 contents) to one layer, one call."""
+    blocks = wl.blocks() if blocks is None else blocks
+    ks, vs = zip(*(wl.kv(layer, b) for b in blocks))
+    k = kv_tensor(np.concatenate(ks), wl.kv_dtype)
+    v = kv_tensor(np.concatenate(vs), wl.kv_dtype)
+    cache.append(layer, blocks, [wl.lengths[b] for b in blocks], k, v)
+    return {b: (kk, vv) for b, kk, vv in zip(blocks, ks, vs)}
+
+
+def oracle_blocks(wl: W.Workload, layer: int):
+    return {b: tuple(np.asarray(x, np.float64) for x in wl.kv(layer, b)) for b in wl.blocks()}
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def max_row_rel(got, ref) -> float:
+    """Largest per-(worker, head) relative L2 error."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return float(np.max(num / den))
+
+
+def decode_np(cache: H.HogwildCache, layer: int, q: np.ndarray):
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(DEV)
+    out, lse = cache.decode(layer, qt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def k_pool_token(cache: H.HogwildCache, layer: int, page: int, head: int, slot: int):
+    """Read one stored key back from the pool using the header's K layout."""
+    d = cache.head_dim
+    g, u = slot // 32, slot % 32
+    base = ((((layer * cache.n_pages + page) * cache.n_kv_heads + head) *
+             (cache.page_size // 32) + g) * 32 * d)
+    idx = [(((i // 32) * 2 + (u // 4) % 2) * 4 + (i % 32) // 8) * 128 + (4 * (u // 8) + u % 4) * 8
+           + i % 8 for i in range(d)]
+    return base + np.array(idx)
+
+
+def v_pool_token(cache: H.HogwildCache, layer: int, page: int, head: int, slot: int):
+    d = cache.head_dim
+    g, u = slot // 32, slot % 32
+    base = ((((layer * cache.n_pages + page) * cache.n_kv_heads + head) *
+             (cache.page_size // 32) + g) * 32 * d)
+    idx = [(((i // 16) * 4 + u // 8) * 16 + i % 16) * 8 + u % 8 for i in range(d)]
+    return base + np.array(idx)

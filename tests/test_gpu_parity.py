@@ -1,0 +1,272 @@
+"""Parity of the gfx950 path against the fp64 oracle, through the C ABI.
+
+Tolerances: relative L2 over all (worker, head, dim) of a layer <= 1e-5 for the
+fp32 configuration and <= 1e-2 for bf16 K/V; the stored pool bytes are
+bit-exact (V copied, K = the oracle's stored-key reference).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hogwild_oracle as O
+from shared_kv_cache_amd import hogwild as H
+from shared_kv_cache_amd import workloads as W
+
+from hw_testlib import (decode_np, fill_layer, k_pool_token, kv_tensor, make_cache, max_row_rel,
+                        oracle_blocks, rel_l2, v_pool_token)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_layer(cache, wl, layer, heads=None, tol=None, offsets=None, q_pos=None, views=None):
+    views = wl.views() if views is None else views
+    q = wl.q(layer)
+    out, lse = decode_np(cache, layer, q)
+    ref, ref_lse = O.concurrent_attention(q.astype(np.float64), oracle_blocks(wl, layer), views,
+                                          offsets=offsets, q_pos=q_pos, theta=wl.theta, heads=heads)
+    hs = list(range(wl.n_q_heads)) if heads is None else list(heads)
+    err = rel_l2(out[:, hs], ref[:, hs])
+    lse_err = float(np.max(np.abs(lse[:, hs] - ref_lse[:, hs])))
+    _say(f"{wl.name} layer {layer}: rel_l2 {err:.3e} max_row {max_row_rel(out[:, hs], ref[:, hs]):.3e} "
+         f"lse_abs {lse_err:.3e}")
+    tol = TOL[wl.kv_dtype] if tol is None else tol
+    assert err <= tol
+    assert lse_err <= max(tol, 1e-6) * 10
+    return out, lse
+
+
+# ------------------------------------------------------------- small configs
+
+def test_tiny_fp32_parity():
+    wl = W.make("tiny_fp32")
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    _check_layer(cache, wl, 0)
+    cache.close()
+
+
+@pytest.mark.parametrize("page_size", [32, 256])
+def test_tiny_fp32_page_sizes_and_splits(page_size):
+    wl = W.make("tiny_fp32", page_size=page_size)
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    outs = []
+    for splits in (1, 3, 11):
+        H.hw_set_split(cache.ctx, splits)
+        outs.append(_check_layer(cache, wl, 0)[0])
+    assert rel_l2(outs[0], outs[2]) <= 1e-6
+    cache.close()
+
+
+def test_pool_bytes_bit_exact_fp32_and_bf16():
+    for name in ("tiny_fp32", "w2_4k"):
+        wl = W.make(name, n_layers=2)
+        cache = make_cache(wl)
+        blocks = fill_layer(cache, wl, 1)
+        torch.cuda.synchronize()
+        kp = cache.k_pool.cpu()
+        vp = cache.v_pool.cpu()
+        if wl.kv_dtype == "bf16":
+            kp = kp.view(torch.int16).numpy().view(np.uint16)
+            vp = vp.view(torch.int16).numpy().view(np.uint16)
+        else:
+            kp, vp = kp.numpy(), vp.numpy()
+        rng = np.random.default_rng(0)
+        for b in wl.blocks():
+            length, pages = cache.block_info(b, 1)
+            assert length == wl.lengths[b]
+            toks = np.unique(np.concatenate([[0, length - 1], rng.integers(0, length, 40)]))
+            k_raw, v_raw = blocks[b]
+            expect_k = O.rope_store_reference(k_raw[toks], toks, wl.theta, wl.kv_dtype)
+            for i, t in enumerate(toks):
+                page, slot = pages[t // wl.page_size], t % wl.page_size
+                for h in range(wl.n_kv_heads):
+                    got_k = kp[k_pool_token(cache, 1, page, h, slot)]
+                    got_v = vp[v_pool_token(cache, 1, page, h, slot)]
+                    np.testing.assert_array_equal(got_k, expect_k[i, h])
+                    want_v = (v_raw[t, h] if wl.kv_dtype == "f32"
+                              else O.bf16_bits_rne(v_raw[t, h]))
+                    np.testing.assert_array_equal(got_v, want_v)
+        _say(f"{name}: pool bytes bit-exact")
+        cache.close()
+
+
+def test_w2_4k_parity_and_split_invariance():
+    wl = W.make("w2_4k", n_layers=2)
+    cache = make_cache(wl)
+    for layer in range(2):
+        fill_layer(cache, wl, layer)
+    cache.set_views(wl.views())
+    for layer in range(2):
+        _check_layer(cache, wl, layer)
+    q = wl.q(1)
+    H.hw_set_split(cache.ctx, 1)
+    o1, l1 = decode_np(cache, 1, q)
+    H.hw_set_split(cache.ctx, 256)
+    o256, l256 = decode_np(cache, 1, q)
+    H.hw_set_split(cache.ctx, 0)
+    _say(f"split 1 vs 256: {rel_l2(o256, o1):.3e}")
+    assert rel_l2(o256, o1) <= 1e-5
+    assert np.max(np.abs(l256 - l1)) <= 1e-4
+    cache.close()
+
+
+def test_page_scatter_invariance_is_bitwise():
+    wl = W.make("w2_4k", n_layers=1)
+    outs = []
+    for seed in (0, 0xABC):
+        cache = make_cache(wl, page_seed=seed, n_pages=2 * wl.n_pages)
+        fill_layer(cache, wl, 0)
+        cache.set_views(wl.views())
+        outs.append(decode_np(cache, 0, wl.q(0)))
+        cache.close()
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_explicit_offsets_gaps_qpos_and_subset_views():
+    wl = W.make("w2_4k", n_layers=1)
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    views = wl.views()
+    L = wl.lengths
+    offsets, q_pos = [], []
+    for v in views:
+        off, acc = [], 7
+        for b in v:
+            off.append(acc)
+            acc += L[b] + 13
+        offsets.append(off)
+        q_pos.append(off[-1] + L[v[-1]] + 2)
+    cache.set_views(views, offsets, q_pos)
+    _check_layer(cache, wl, 0, offsets=offsets, q_pos=q_pos, views=views)
+    # no-sync style: each worker sees the common block and its own block only
+    sub = [[wl.history[0], wl.inprogress[w]] for w in range(wl.n_workers)]
+    cache.set_views(sub)
+    _check_layer(cache, wl, 0, views=sub)
+    cache.close()
+
+
+def test_many_rows_multiple_row_blocks_and_empty_view():
+    # 5 workers x G = 16 rows each = 80 rows: two row blocks of the decode grid
+    wl = W.make("tiny_fp32")
+    wl = W.Workload(**{**wl.__dict__, "name": "rows80", "n_workers": 5, "n_q_heads": 32,
+                       "n_kv_heads": 2, "kv_dtype": "bf16",
+                       "inprogress": [1, 2, 3, 4, 5],
+                       "lengths": {0: 300, 1: 33, 2: 1, 3: 64, 4: 65, 5: 0},
+                       "owners": {0: -1, 1: 0, 2: 1, 3: 2, 4: 3, 5: 4}, "n_pages": 40})
+    cache = make_cache(wl, max_blocks=8)
+    fill_layer(cache, wl, 0, blocks=[0, 1, 2, 3, 4])
+    views = wl.views()
+    views[4] = [5]                                 # a worker whose view holds no token
+    cache.set_views(views)
+    q = wl.q(0)
+    out, lse = decode_np(cache, 0, q)
+    assert np.all(out[4] == 0.0) and np.all(np.isneginf(lse[4]))
+    blocks = {b: tuple(np.asarray(x, np.float64) for x in wl.kv(0, b)) for b in range(6)}
+    ref, ref_lse = O.concurrent_attention(q[:4].astype(np.float64), blocks, views[:4], theta=wl.theta)
+    err = rel_l2(out[:4], ref)
+    _say(f"rows80: rel_l2 {err:.3e}")
+    assert err <= 1e-2
+    cache.close()
+
+
+def test_errors_leave_gpu_state_unchanged():
+    wl = W.make("w2_4k", n_layers=1)
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    before = decode_np(cache, 0, wl.q(0))
+    free0 = H.hw_free_pages(cache.ctx)
+    big = torch.zeros((free0 * wl.page_size + 1, wl.n_kv_heads, wl.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    with pytest.raises(H.HwError) as e:
+        cache.append(0, [wl.inprogress[0]], [big.shape[0]], big, big)
+    assert e.value.status == H.HW_ERR_OUT_OF_PAGES
+    with pytest.raises(H.HwError) as e:
+        cache.set_views([[0, 0]])
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    bad_off = [[0, 10, 20]] * wl.n_workers
+    cache.set_views(wl.views(), bad_off)
+    with pytest.raises(H.HwError) as e:
+        cache.decode(0, torch.from_numpy(wl.q(0)).cuda())
+    assert e.value.status == H.HW_ERR_STALE_VIEW
+    cache.set_views(wl.views())
+    after = decode_np(cache, 0, wl.q(0))
+    assert H.hw_free_pages(cache.ctx) == free0
+    np.testing.assert_array_equal(before[0], after[0])
+    cache.close()
+
+
+# ------------------------------------------------------- full-size configs
+
+def test_w4_16k_parity_sampled_layers():
+    wl = W.make("w4_16k")                 # 64 layers, as timed
+    cache = make_cache(wl)
+    for layer in range(wl.n_layers):
+        fill_layer(cache, wl, layer)
+    cache.set_views(wl.views())
+    for layer in (0, 21, 42, 63):
+        _check_layer(cache, wl, layer)
+    cache.close()
+
+
+def test_w8_32k_parity_across_steps():
+    steps = 3
+    wl = W.make("w8_32k", steps=steps)
+    cache = make_cache(wl)
+    for layer in range(wl.n_layers):
+        fill_layer(cache, wl, layer)
+    lengths = dict(wl.lengths)
+    hist = {layer: {} for layer in (0, 5)}
+    for step in range(1, steps + 1):
+        cache.set_views(wl.views())
+        for layer in range(wl.n_layers):
+            k, v = wl.step_kv(layer, step)
+            cache.append(layer, wl.inprogress, [1] * wl.n_workers, kv_tensor(k, "bf16"),
+                         kv_tensor(v, "bf16"))
+            if layer in hist:
+                hist[layer][step] = (k, v)
+        for b in wl.inprogress:
+            lengths[b] += 1
+        for layer in (0, 5):
+            blocks = {}
+            for b in wl.blocks():
+                k0, v0 = wl.kv(layer, b)
+                if b in wl.inprogress:
+                    w = wl.inprogress.index(b)
+                    k0 = np.concatenate([k0] + [hist[layer][s][0][w:w + 1] for s in range(1, step + 1)])
+                    v0 = np.concatenate([v0] + [hist[layer][s][1][w:w + 1] for s in range(1, step + 1)])
+                blocks[b] = (k0.astype(np.float64), v0.astype(np.float64))
+            q = wl.q(layer, step)
+            out, lse = decode_np(cache, layer, q)
+            ref, ref_lse = O.concurrent_attention(q.astype(np.float64), blocks, wl.views(), theta=wl.theta)
+            err = rel_l2(out, ref)
+            _say(f"w8_32k step {step} layer {layer}: rel_l2 {err:.3e}")
+            assert err <= 1e-2
+    cache.close()
+
+
+def test_w4_128k_sinks_split256_sampled_heads():
+    wl = W.make("w4_128k_sinks", n_layers=1)
+    cache = make_cache(wl, max_splits=512)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    H.hw_set_split(cache.ctx, 256)
+    assert H.hw_debug_resolve(cache.ctx, 0, wl.n_workers)["n_splits"] == 256
+    rng = np.random.default_rng(wl.seed)
+    heads = sorted(set(int(x) for x in rng.choice(35, size=3, replace=False)) |
+                   {int(rng.integers(35, 40))})
+    _check_layer(cache, wl, 0, heads=heads)
+    cache.close()

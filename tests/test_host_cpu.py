@@ -1,0 +1,356 @@
+"""Host logic of the C-ABI library, checked on a machine without a GPU.
+
+The library is loaded through its C ABI; only host-only entry points are
+called (no kernel launches, no device memory). Slot assignment, page
+allocation and view resolution are compared bit-exactly with a small Python
+model written here from the header's specification, and every error path is
+forced from the host and shown to leave the state unchanged.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import hogwild_oracle as O
+from shared_kv_cache_amd import hogwild as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_K, FAKE_V = 1 << 20, 2 << 20       # never dereferenced by host-only calls
+
+
+def make_cfg(**kw):
+    base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=64, n_pages=16,
+                max_blocks=16, max_workers=4, max_position=4096, max_splits=0,
+                kv_dtype=H.HW_BF16, page_seed=0, rope_theta=1e4, softmax_scale=0.0,
+                k_pool=FAKE_K, v_pool=FAKE_V)
+    base.update(kw)
+    return H.HwConfig(**base)
+
+
+@pytest.fixture
+def ctx():
+    c = H.hw_create(make_cfg())
+    yield c
+    H.hw_destroy(c)
+
+
+# ------------------------------------------------------------------- exports
+
+def test_library_exports_every_declared_symbol():
+    lib = H.load_library()
+    declared = set()
+    for name in ("hogwild.h", "hogwild_debug.h"):
+        text = open(os.path.join(ROOT, "include", name)).read()
+        declared |= set(re.findall(r"\b(hw_[a-z_]+)\s*\(", text))
+    assert declared == set(H.EXPORTS)
+    for sym in declared:
+        assert hasattr(lib, sym), sym          # dlsym succeeds
+
+
+# ----------------------------------------------------------------- creation
+
+@pytest.mark.parametrize("field,value", [
+    ("n_layers", 0), ("n_q_heads", 7), ("n_kv_heads", 0), ("head_dim", 96), ("page_size", 48),
+    ("n_pages", 0), ("max_blocks", 0), ("max_workers", 0), ("max_position", 0),
+    ("max_splits", -1), ("kv_dtype", 7), ("rope_theta", 1.0), ("softmax_scale", -1.0),
+    ("k_pool", 0), ("v_pool", FAKE_V + 8),
+])
+def test_create_rejects_bad_config(field, value):
+    with pytest.raises(H.HwError) as e:
+        H.hw_create(make_cfg(**{field: value}))
+    assert e.value.status == H.HW_ERR_INVALID_ARG and e.value.message
+
+
+def test_workspace_size_formula(ctx):
+    d, half, max_pos = 128, 64, 4096
+    al = lambda x: (x + 255) // 256 * 256
+    max_groups = 16 * (64 // 32)
+    rows = 4 * 4
+    expect = al(max_pos * half * 8)
+    expect += al(al(16 * 4 * 4) + al(max_groups * 8))
+    expect += al(256 * 2 * rows * d * 4)
+    expect += al(256 * 2 * rows * 4)
+    assert H.hw_workspace_bytes(ctx) == expect
+
+
+def test_calls_without_workspace_or_views(ctx):
+    with pytest.raises(H.HwError) as e:
+        H.hw_append_kv(ctx, 0, [0], [4], FAKE_K, FAKE_V, 0)
+    assert e.value.status == H.HW_ERR_WORKSPACE
+    with pytest.raises(H.HwError) as e:
+        H.hw_concurrent_decode(ctx, 0, FAKE_K, FAKE_V, None, 0)
+    assert e.value.status == H.HW_ERR_WORKSPACE
+    with pytest.raises(H.HwError) as e:
+        H.hw_debug_resolve(ctx, 0, 1)
+    assert e.value.status == H.HW_ERR_STALE_VIEW
+
+
+# ------------------------------------------------------ page allocation model
+
+def splitmix_shuffle(n, seed):
+    """Fisher-Yates over 0..n-1 driven by splitmix64 (Steele, Lea, Flood)."""
+    mask = (1 << 64) - 1
+    state = seed
+    order = list(range(n))
+    for i in range(n - 1, 0, -1):
+        state = (state + 0x9E3779B97F4A7C15) & mask
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & mask
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & mask
+        z ^= z >> 31
+        j = z % (i + 1)
+        order[i], order[j] = order[j], order[i]
+    return order
+
+
+class HostModel:
+    """Python model of the header's slot-assignment and page rules."""
+
+    def __init__(self, n_layers, page_size, n_pages, seed):
+        order = splitmix_shuffle(n_pages, seed) if seed else list(range(n_pages))
+        self.free = list(reversed(order))       # pop() hands out order[0] first
+        self.ps = page_size
+        self.n_layers = n_layers
+        self.pages, self.len = {}, {}
+
+    def reserve(self, layer, ids, counts):
+        runs, row = [], 0
+        need_total = 0
+        for b, n in zip(ids, counts):
+            lens = self.len.setdefault(b, [0] * self.n_layers)
+            pages = self.pages.setdefault(b, [])
+            need = -(-max(max(lens), lens[layer] + n) // self.ps)
+            need_total += max(0, need - len(pages))
+        if need_total > len(self.free):
+            return None
+        for b, n in zip(ids, counts):
+            lens, pages = self.len[b], self.pages[b]
+            need = -(-max(max(lens), lens[layer] + n) // self.ps)
+            while len(pages) < need:
+                pages.append(self.free.pop())
+            pos, left = lens[layer], n
+            while left:
+                slot = pos % self.ps
+                cnt = min(left, self.ps - slot)
+                runs.append((row, pages[pos // self.ps], slot, cnt, pos))
+                row, pos, left = row + cnt, pos + cnt, left - cnt
+            lens[layer] += n
+        return runs
+
+    def reset(self, b):
+        for p in reversed(self.pages.get(b, [])):
+            self.free.append(p)
+        self.pages[b] = []
+        self.len[b] = [0] * self.n_layers
+
+
+@pytest.mark.parametrize("seed", [0, 1, 0xDEADBEEF])
+def test_slot_assignment_and_pages_bit_exact(seed):
+    cfg = make_cfg(n_pages=40, page_size=64, page_seed=seed, max_blocks=8)
+    c = H.hw_create(cfg)
+    model = HostModel(2, 64, 40, seed)
+    rng = np.random.default_rng(seed)
+    try:
+        for step in range(60):
+            layer = int(rng.integers(0, 2))
+            k = int(rng.integers(1, 4))
+            ids = [int(x) for x in rng.choice(8, size=k, replace=False)]
+            counts = [int(x) for x in rng.integers(0, 90, size=k)]
+            expect = model.reserve(layer, ids, counts)
+            if expect is None:
+                free0 = H.hw_free_pages(c)
+                with pytest.raises(H.HwError) as e:
+                    H.hw_debug_reserve(c, layer, ids, counts)
+                assert e.value.status == H.HW_ERR_OUT_OF_PAGES
+                assert H.hw_free_pages(c) == free0
+                victim = ids[0]
+                model.reset(victim)
+                H.hw_reset_block(c, victim)
+                continue
+            got = H.hw_debug_reserve(c, layer, ids, counts)
+            assert got == expect
+            assert H.hw_free_pages(c) == len(model.free)
+            for b in ids:
+                for lay in range(2):
+                    length, pages = H.hw_block_info(c, b, lay)
+                    assert length == model.len[b][lay] and pages == model.pages[b]
+    finally:
+        H.hw_destroy(c)
+
+
+def test_scattered_pages_are_a_permutation():
+    c = H.hw_create(make_cfg(n_pages=64, page_size=32, page_seed=0x5EED, max_blocks=2))
+    runs = H.hw_debug_reserve(c, 0, [0], [64 * 32])
+    pages = [r[1] for r in runs]
+    assert sorted(pages) == list(range(64)) and pages != list(range(64))
+    assert pages == splitmix_shuffle(64, 0x5EED)
+    H.hw_destroy(c)
+
+
+@pytest.mark.parametrize("ids,counts,status", [
+    ([16], [1], H.HW_ERR_INVALID_ARG),           # id out of range
+    ([-1], [1], H.HW_ERR_INVALID_ARG),
+    ([3, 3], [1, 1], H.HW_ERR_INVALID_ARG),      # repeated id
+    ([2], [-1], H.HW_ERR_INVALID_ARG),           # negative count
+    ([2], [4097], H.HW_ERR_INVALID_ARG),         # reaches max_position
+    ([2, 3], [600, 600], H.HW_ERR_OUT_OF_PAGES), # 10 + 10 pages > 16
+])
+def test_append_errors_leave_state_unchanged(ctx, ids, counts, status):
+    H.hw_debug_reserve(ctx, 0, [5], [70])
+    before = (H.hw_free_pages(ctx), H.hw_block_info(ctx, 5, 0), H.hw_block_info(ctx, 2, 0))
+    with pytest.raises(H.HwError) as e:
+        H.hw_debug_reserve(ctx, 0, ids, counts)
+    assert e.value.status == status
+    assert (H.hw_free_pages(ctx), H.hw_block_info(ctx, 5, 0), H.hw_block_info(ctx, 2, 0)) == before
+    with pytest.raises(H.HwError):
+        H.hw_debug_reserve(ctx, 2, [1], [1])      # layer out of range
+
+
+def test_pages_shared_across_layers(ctx):
+    r0 = H.hw_debug_reserve(ctx, 0, [1], [100])   # 2 pages
+    r1 = H.hw_debug_reserve(ctx, 1, [1], [30])    # same pages, no new ones
+    assert [r[1] for r in r1] == [r0[0][1]] and H.hw_free_pages(ctx) == 14
+    r2 = H.hw_debug_reserve(ctx, 1, [1], [100])   # layer 1 grows to 130 -> 3rd page
+    assert H.hw_free_pages(ctx) == 13
+    assert r2[0][1:] == (r0[0][1], 30, 34, 30) and r2[1][2:] == (0, 64, 64) and r2[2][2:] == (0, 2, 128)
+
+
+# ------------------------------------------------------------- view model
+
+def model_resolve(lengths, pages, views, offsets, q_pos, page_size, max_position):
+    """Python model of the resolution specified in hogwild_debug.h."""
+    n = len(views)
+    segs = []
+    all_offs, all_q = [], []
+    for w, v in enumerate(views):
+        offs = offsets[w] if offsets is not None else O.default_offsets(v, lengths)
+        if q_pos is not None:
+            qp = q_pos[w]
+        else:
+            qp = offs[-1] + lengths[v[-1]] - 1 if v else -1
+        err = O.view_error(v, offs, lengths, qp)
+        if err:
+            return err
+        for b, o in zip(v, offs):
+            if lengths[b] and qp - o >= max_position:
+                return "delta"
+        all_offs.append(offs)
+        all_q.append(qp)
+        for b in v:
+            if lengths[b] > 0 and b not in segs:
+                segs.append(b)
+    delta = [[-1] * n for _ in segs]
+    for w, v in enumerate(views):
+        for b, o in zip(v, all_offs[w]):
+            if b in segs:
+                delta[segs.index(b)][w] = all_q[w] - o
+    groups = []
+    for s, b in enumerate(segs):
+        for t in range(0, lengths[b], 32):
+            groups.append((pages[b][t // page_size], (t % page_size) // 32, s, min(32, lengths[b] - t)))
+    return segs, delta, groups
+
+
+def _fill(c, layer, lens):
+    for b, n in lens.items():
+        if n:
+            H.hw_debug_reserve(c, layer, [b], [n])
+
+
+def _pages_of(c, blocks, layer=0):
+    info = {b: H.hw_block_info(c, b, layer) for b in blocks}
+    return {b: i[0] for b, i in info.items()}, {b: i[1] for b, i in info.items()}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_resolution_bit_exact(seed):
+    rng = np.random.default_rng(50 + seed)
+    c = H.hw_create(make_cfg(n_pages=64, page_size=64, max_blocks=12, max_workers=4,
+                             page_seed=seed))
+    try:
+        n = int(rng.integers(1, 5))
+        history = [0, 1, 2]
+        inprog = [3 + w for w in range(n)]
+        lens = {b: int(rng.integers(1, 200)) for b in history}
+        lens.update({b: int(rng.integers(0 if w else 1, 70)) for w, b in enumerate(inprog)})
+        _fill(c, 0, lens)
+        views = [O.canonical_view(w, history, inprog) for w in range(n)]
+        lengths, pages = _pages_of(c, history + inprog)
+        offsets = q_pos = None
+        if seed % 2:        # explicit offsets with gaps and a later query
+            offsets = []
+            for v in views:
+                acc, off = int(rng.integers(0, 5)), []
+                for b in v:
+                    off.append(acc)
+                    acc += lengths[b] + int(rng.integers(0, 9))
+                offsets.append(off)
+            q_pos = [offsets[w][-1] + lengths[v[-1]] + int(rng.integers(0, 3)) for w, v in enumerate(views)]
+        H.hw_set_views(c, views, offsets, q_pos)
+        got = H.hw_debug_resolve(c, 0, n)
+        segs, delta, groups = model_resolve(lengths, pages, views, offsets, q_pos, 64, 4096)
+        assert got["segs"] == segs and got["delta"] == delta and got["groups"] == groups
+        assert got["n_groups"] == len(groups)
+        # layer 1 holds nothing yet: every view is empty there
+        empty = H.hw_debug_resolve(c, 1, n)
+        assert empty["n_groups"] == 0 and empty["n_segs"] == 0
+    finally:
+        H.hw_destroy(c)
+
+
+def test_subset_views_and_visibility(ctx):
+    _fill(ctx, 0, {0: 40, 1: 10, 2: 12})
+    # worker 0 sees only the common block and its own (no-sync style view)
+    H.hw_set_views(ctx, [[0, 1], [0, 1, 2]])
+    got = H.hw_debug_resolve(ctx, 0, 2)
+    assert got["segs"] == [0, 1, 2]
+    assert got["delta"] == [[49, 61], [9, 21], [-1, 11]]
+
+
+@pytest.mark.parametrize("offsets,q_pos,why", [
+    ([[0, 30, 40]], None, "overlapping blocks"),
+    ([[0, 40, 50]], [55], "key after query"),
+    ([[0, 40, 4000]], [4100], "delta"),
+])
+def test_stale_views_rejected_like_the_oracle(ctx, offsets, q_pos, why):
+    _fill(ctx, 0, {0: 40, 1: 10, 2: 12})
+    H.hw_set_views(ctx, [[0, 1, 2]], offsets, q_pos)
+    lengths, pages = _pages_of(ctx, [0, 1, 2])
+    assert model_resolve(lengths, pages, [[0, 1, 2]], offsets, q_pos, 64, 4096) == why
+    with pytest.raises(H.HwError) as e:
+        H.hw_debug_resolve(ctx, 0, 1)
+    assert e.value.status == H.HW_ERR_STALE_VIEW
+
+
+@pytest.mark.parametrize("views,offsets,q_pos", [
+    ([[0, 0]], None, None),                   # repeated block
+    ([[0, 99]], None, None),                  # id out of range
+    ([[0]] * 5, None, None),                  # more workers than max_workers
+    ([[0, 1]], [[0, -4]], None),              # negative offset
+    ([[0, 1]], None, [-2]),                   # bad q_pos
+    ([], None, None),                         # no workers
+])
+def test_set_views_rejects_bad_input(ctx, views, offsets, q_pos):
+    H.hw_set_views(ctx, [[0]])
+    with pytest.raises(H.HwError) as e:
+        H.hw_set_views(ctx, views, offsets, q_pos)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    _fill(ctx, 0, {0: 5})
+    assert H.hw_debug_resolve(ctx, 0, 1)["segs"] == [0]      # previous views kept
+
+
+def test_split_choice_and_override(ctx):
+    _fill(ctx, 0, {0: 900, 1: 24})
+    H.hw_set_views(ctx, [[0, 1]])
+    auto = H.hw_debug_resolve(ctx, 0, 1)["n_splits"]
+    # 30 groups: min(ceil(256 CUs / (2 KV heads * 1 row block)), 30 // 8) without a GPU
+    assert auto == 3
+    H.hw_set_split(ctx, 7)
+    assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == 7
+    with pytest.raises(H.HwError):
+        H.hw_set_split(ctx, 257)
+    H.hw_set_split(ctx, 0)
+    assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == auto
