@@ -213,7 +213,10 @@ class HogwildCache:
         self.kv_torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[kv_dtype]
         self.n_layers, self.n_q_heads, self.n_kv_heads = n_layers, n_q_heads, n_kv_heads
         self.head_dim, self.page_size, self.n_pages = head_dim, page_size, n_pages
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         elems = n_layers * n_pages * n_kv_heads * page_size * head_dim
         self.k_pool = torch.zeros(elems, dtype=self.kv_torch_dtype, device=self.device)
         self.v_pool = torch.zeros(elems, dtype=self.kv_torch_dtype, device=self.device)

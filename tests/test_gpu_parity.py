@@ -117,7 +117,9 @@ def test_w2_4k_parity_and_split_invariance():
     o256, l256 = decode_np(cache, 1, q)
     H.hw_set_split(cache.ctx, 0)
     _say(f"split 1 vs 256: {rel_l2(o256, o1):.3e}")
-    assert rel_l2(o256, o1) <= 1e-5
+    # Each partition rounds its probabilities to bf16 against its own running max, so
+    # split counts differ at the bf16 level (the fp32 pool case above agrees to 1e-6).
+    assert rel_l2(o256, o1) <= TOL["bf16"]
     assert np.max(np.abs(l256 - l1)) <= 1e-4
     cache.close()
 
