@@ -1,7 +1,8 @@
 /*
  * hogwild_debug.h -- host-only introspection of the Hogwild! decode library, for tests.
  *
- * These calls touch no GPU and enqueue nothing, so the host logic (slot assignment, page
+ * Apart from the two profiling hooks at the end, these calls touch no GPU and enqueue
+ * nothing, so the host logic (slot assignment, page
  * allocation, view resolution, validation) can be checked bit-exactly on a machine without
  * a GPU. Same status codes and validation rules as hogwild.h.
  */
@@ -37,6 +38,17 @@ hw_status hw_debug_reserve(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const i
 hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *delta,
                            int32_t cap_segs, int32_t *n_segs, int32_t *groups,
                            int32_t cap_groups, int32_t *n_groups, int32_t *n_splits);
+
+/* ---- profiling hooks (these two do call HIP) ---------------------------------------------
+ * With capacity > 0, each following hw_concurrent_decode records a HIP event pair on its
+ * stream around its concurrent_decode kernel (not the split merge that follows it), for up to
+ * `capacity` calls; capacity 0 stops recording and frees the events. Errors: HW_ERR_HIP. */
+hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity);
+
+/* Wait for the recorded events and write, per recorded call i < cap, decode_ms[i]: the
+ * duration of that call's concurrent_decode kernel. *n receives the number of recorded
+ * calls; recording then restarts at zero. */
+hw_status hw_debug_kernel_elapsed(hw_ctx *ctx, float *decode_ms, int32_t cap, int32_t *n);
 
 #ifdef __cplusplus
 }

@@ -78,7 +78,8 @@ struct hw_ctx {
   // device workspace carve-up
   void *ws = nullptr;
   size_t ws_bytes = 0;
-  size_t off_trig = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0, tables_bytes = 0;
+  size_t off_trig = 0, off_freq = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0;
+  size_t tables_bytes = 0;
   size_t part_o_bytes = 0, part_lse_bytes = 0, total_bytes = 0;
 
   // upload cache
@@ -93,6 +94,10 @@ struct hw_ctx {
   bool event_live[kStagingSlots] = {};
   int next_slot = 0;
   bool debug_sync = false;
+
+  // profiling hooks: two events per recorded decode call
+  std::vector<hipEvent_t> prof_events;
+  int32_t prof_capacity = 0, prof_count = 0;
 
   hw_status fail(hw_status s, const std::string &m) {
     err = m;
@@ -123,6 +128,8 @@ void layout_workspace(hw_ctx *c) {
   size_t off = 0;
   c->off_trig = off;
   off = align_up(off + (size_t)g.max_position * half * 2 * sizeof(float));
+  c->off_freq = off;
+  off = align_up(off + half * sizeof(double));
   c->off_tables = off;
   c->tables_bytes = align_up((size_t)g.max_blocks * g.max_workers * sizeof(int32_t)) +
                     align_up(max_groups * 2 * sizeof(int32_t));
@@ -242,8 +249,13 @@ void commit_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *id
 
 // ---- view resolution ---------------------------------------------------------------
 
+int32_t row_blocks_for(const hw_ctx *c, int32_t n_workers) {
+  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
+  return std::max(1, (rows_total(c, n_workers) + rpb - 1) / rpb);
+}
+
 int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
-  const int32_t row_blocks = (rows_total(c, n_workers) + hw::kRowsPerBlock - 1) / hw::kRowsPerBlock;
+  const int32_t row_blocks = row_blocks_for(c, n_workers);
   const int32_t per_head = c->cfg.n_kv_heads * std::max(1, row_blocks);
   int32_t s = (c->num_cus + per_head - 1) / per_head;
   s = std::min(s, std::max(1, n_groups / 8));
@@ -420,6 +432,7 @@ hw_status hw_create(const hw_config *cfg, hw_ctx **out) {
 
 hw_status hw_destroy(hw_ctx *ctx) {
   if (!ctx) return HW_OK;
+  for (hipEvent_t e : ctx->prof_events) (void)hipEventDestroy(e);
   for (int i = 0; i < kStagingSlots; ++i)
     if (ctx->events[i]) (void)hipEventDestroy(ctx->events[i]);
   if (ctx->staging) (void)hipHostFree(ctx->staging);
@@ -458,6 +471,12 @@ hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes) {
   hipError_t e = hipMemcpy((char *)dev + ctx->off_trig, table.data(), table.size() * sizeof(float),
                            hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(rope table)");
+  // Query rotations: theta_j / (2 pi) in fp64, the rotation in turns per position.
+  std::vector<double> turns(half);
+  for (int j = 0; j < half; ++j) turns[j] = inv[j] / (2.0 * 3.14159265358979323846);
+  e = hipMemcpy((char *)dev + ctx->off_freq, turns.data(), turns.size() * sizeof(double),
+                hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(turn frequencies)");
   int dev_id = 0;
   if (hipGetDevice(&dev_id) == hipSuccess) {
     int cus = 0;
@@ -624,7 +643,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.lse = lse;
   a.groups = reinterpret_cast<const int2 *>(tables + ctx->up_groups_off);
   a.delta = reinterpret_cast<const int32_t *>(tables);
-  a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
+  a.turn_freq = reinterpret_cast<const double *>((char *)ctx->ws + ctx->off_freq);
   a.part_o = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_o);
   a.part_lse = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_lse);
   a.n_groups = n_groups;
@@ -635,11 +654,23 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.rows = rows;
   a.n_splits = splits;
   a.page_groups = g.page_size / hw::kTokGroup;
+  a.rows_per_block = hw::rows_per_block(g.kv_dtype);
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
-  const int32_t row_blocks = (rows + hw::kRowsPerBlock - 1) / hw::kRowsPerBlock;
+  const int32_t row_blocks = row_blocks_for(ctx, n);
+  const bool prof = ctx->prof_count < ctx->prof_capacity;
+  hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
+  if (prof) {
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord(profile)");
+  }
   hw_status st = post_launch(ctx, hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s),
                              "concurrent_decode", s);
   if (st != HW_OK) return st;
+  if (prof) {
+    hipError_t e = hipEventRecord(ev[1], s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord(profile)");
+    ctx->prof_count++;
+  }
   if (splits > 1) {
     hw::MergeArgs m{};
     m.part_o = a.part_o;
@@ -655,6 +686,42 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     st = post_launch(ctx, hw::launch_merge(g.head_dim, m, s), "lse_merge", s);
     if (st != HW_OK) return st;
   }
+  return HW_OK;
+}
+
+hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (capacity < 0) return ctx->fail(HW_ERR_INVALID_ARG, "capacity < 0");
+  for (hipEvent_t e : ctx->prof_events) (void)hipEventDestroy(e);
+  ctx->prof_events.clear();
+  ctx->prof_capacity = ctx->prof_count = 0;
+  for (int32_t i = 0; i < 2 * capacity; ++i) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      for (hipEvent_t x : ctx->prof_events) (void)hipEventDestroy(x);
+      ctx->prof_events.clear();
+      return hip_fail(ctx, err, "hipEventCreate(profile)");
+    }
+    ctx->prof_events.push_back(e);
+  }
+  ctx->prof_capacity = capacity;
+  return HW_OK;
+}
+
+hw_status hw_debug_kernel_elapsed(hw_ctx *ctx, float *decode_ms, int32_t cap, int32_t *n) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  if (n) *n = ctx->prof_count;
+  for (int32_t i = 0; i < ctx->prof_count && i < cap; ++i) {
+    hipEvent_t *ev = &ctx->prof_events[2 * (size_t)i];
+    hipError_t e = hipEventSynchronize(ev[1]);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventSynchronize(profile)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventElapsedTime(profile)");
+    if (decode_ms) decode_ms[i] = ms;
+  }
+  ctx->prof_count = 0;
   return HW_OK;
 }
 

@@ -12,6 +12,9 @@ namespace hw {
 constexpr int kTokGroup = 32;          // tokens per pool group (one MFMA K/V tile)
 constexpr int kWaves = 4;              // waves per decode workgroup
 constexpr int kRowsPerBlock = 64;      // stacked (worker, query head) rows per decode workgroup
+constexpr int kRowsPerBlockF32 = 32;   // the same for fp32 pools (their operands are twice as wide)
+
+inline int rows_per_block(hw_dtype dt) { return dt == HW_F32 ? kRowsPerBlockF32 : kRowsPerBlock; }
 constexpr int kMaxRunsPerLaunch = 64;  // append runs carried in one launch's arguments
 
 // One run of appended tokens: consecutive tokens of one block inside one page.
@@ -43,7 +46,7 @@ struct DecodeArgs {
   float *lse;              // [n_workers][n_q_heads] or null      (idem)
   const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens}
   const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
-  const float2 *trig;      // [max_position][head_dim/2]
+  const double *turn_freq; // [head_dim/2] theta^(-2j/d) / (2 pi): rotation turns per position
   float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
   float *part_lse;         // [n_splits][n_kv_heads][rows] log2-domain partial normalisers
   int32_t n_groups;
@@ -54,9 +57,12 @@ struct DecodeArgs {
   int32_t rows;            // n_workers * group
   int32_t n_splits;
   int32_t page_groups;
+  int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)
   float q_scale;           // softmax_scale * log2(e)
 };
 
+
+hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStream_t s);
 struct MergeArgs {
   const float *part_o;
   const float *part_lse;
@@ -70,9 +76,8 @@ struct MergeArgs {
   int32_t n_splits;
 };
 
-hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStream_t s);
+hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
                          hipStream_t s);
-hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
 
 }  // namespace hw

@@ -252,176 +252,295 @@ struct Frag<float, D> {
   }
 };
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one row: gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange rows of 16 lanes without the LDS path.
 __device__ __forceinline__ float wave_max_across_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// The running max is only raised (and the accumulators rescaled) when a row's new scores
+// exceed it by more than this many doublings; otherwise probabilities are taken against the
+// stale max and stay below 2^8, well inside bf16 and fp32 range.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Per-wave pipeline state: one 32-token group's operands, its descriptor (wave-uniform) and
+// the query offsets of the lane's rows for the group's block.
+template <typename KV, int D, int RT>
+struct Stage {
+  Frag<KV, D> f;
+  int desc_x, desc_y;
+  int delta[RT];
+};
+
+// A wave's group descriptors, 64 at a time: lane j holds descriptor base + j. One vector
+// load replaces a dependent scalar load per group.
+struct DescBatch {
+  long long base;
+  int x, y;
+};
+
+__device__ __forceinline__ void load_desc_batch(DescBatch &db, const int2 *groups, long long base,
+                                                long long end, int lane) {
+  db.base = base;
+  int2 d = make_int2(0, 0);
+  if (base + lane < end) d = groups[base + lane];
+  db.x = d.x;
+  db.y = d.y;
+}
+
+template <typename KV, int D, int RT>
+__device__ __forceinline__ void fetch_group(Stage<KV, D, RT> &st, DescBatch &db,
+                                            const DecodeArgs &a, const KV *kl, const KV *vl,
+                                            size_t head_groups, long long g, long long we,
+                                            const int *row_w, int lane) {
+  if (g - db.base >= 64) load_desc_batch(db, a.groups, db.base + 64, we, lane);
+  const int j = (int)(g - db.base);
+  st.desc_x = __builtin_amdgcn_readlane(db.x, j);
+  st.desc_y = __builtin_amdgcn_readlane(db.y, j);
+  const int seg = st.desc_y >> 8;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) st.delta[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
+  const size_t gb = ((size_t)st.desc_x + head_groups) * (size_t)(32 * D);
+  st.f.load(kl + gb, vl + gb, lane);
+}
+
+__device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <typename KV, int D, int RT>
 __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
+  using S = Stage<KV, D, RT>;
+  using QOp = typename F::QOp;
   constexpr int NC = F::NC, NDT = F::NDT;
+  // Pipeline stages per wave (NST - 1 groups in flight), as many as the registers allow.
+  constexpr int NST = (RT <= 2 && sizeof(KV) == 2) ? 3 : 2;
   constexpr int QSTRIDE = D + 4;                   // padded q row (LDS bank spread)
   constexpr int Q_FLOATS = RT * 16 * QSTRIDE;
-  constexpr int BUF_F4 = RT * NDT * 64;            // one wave's O^T in lane layout
-  constexpr int M_FLOATS = 2 * BUF_F4 * 4;
-  constexpr int SMEM = Q_FLOATS > M_FLOATS ? Q_FLOATS : M_FLOATS;
+  constexpr int QOP_FLOATS = kWaves * RT * NC * 64 * (int)(sizeof(QOp) / 4);
+  constexpr int SLOTS = RT * NDT * 64;             // one wave's O^T, f32x4 slots in lane order
+  constexpr int M_FLOATS = kWaves * SLOTS * 4;
+  constexpr int SMEM = Q_FLOATS + QOP_FLOATS > M_FLOATS ? Q_FLOATS + QOP_FLOATS : M_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ double sm_freq[D / 2];
   __shared__ float sm_m[kWaves][64];
   __shared__ float sm_l[kWaves][64];
+  __shared__ float sm_rowm[64], sm_rowl[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_slot();
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y;
-  const int row0 = blockIdx.z * kRowsPerBlock;
-  const int nrows = min(kRowsPerBlock, a.rows - row0);
+  const int row0 = blockIdx.z * a.rows_per_block;
+  const int nrows = min(a.rows_per_block, a.rows - row0);
+  // Rotated query operands of this wave, in lane order: [rt][chunk][lane].
+  QOp *qop_lds = reinterpret_cast<QOp *>(smem + Q_FLOATS) + (size_t)wave * RT * NC * 64;
 
-  // Stage this workgroup's raw query rows, pre-scaled by softmax_scale * log2(e).
-  for (int i = tid; i < RT * 16 * D; i += 256) {
-    const int r = i / D, d = i % D;
-    float val = 0.0f;
-    if (r < nrows) {
-      const int rr = row0 + r;
-      const int w = rr / a.group, gq = rr % a.group;
-      val = a.q[((size_t)w * a.n_q_heads + kvh * a.group + gq) * D + d] * a.q_scale;
-    }
-    smem[r * QSTRIDE + d] = val;
-  }
-  __syncthreads();
-
+  // This workgroup's range of token groups, cut into one contiguous range per wave.
   const long long begin = (long long)split * a.n_groups / a.n_splits;
   const long long end = (long long)(split + 1) * a.n_groups / a.n_splits;
+  const long long wb = begin + (end - begin) * wave / kWaves;
+  const long long we = begin + (end - begin) * (wave + 1) / kWaves;
   const KV *kl = static_cast<const KV *>(a.k_layer);
   const KV *vl = static_cast<const KV *>(a.v_layer);
   const size_t head_groups = (size_t)kvh * a.page_groups;
 
+  int row_w[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + col;
+    row_ok[rt] = r < nrows;
+    row_w[rt] = row_ok[rt] ? (row0 + r) / a.group : 0;
+  }
+
+  // Issue order: descriptors, raw queries, then the first groups' K/V, so that waiting for
+  // the older loads leaves the K/V loads in flight.
+  DescBatch db;
+  load_desc_batch(db, a.groups, wb, we, lane);
+  constexpr int QPT = (RT * 16 * D + 255) / 256;   // query values per thread
+  float qv[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * 256;
+    const int r = i / D, d = i % D;
+    qv[k] = 0.0f;
+    if (i < RT * 16 * D && r < nrows) {
+      const int rr = row0 + r;
+      const int w = rr / a.group, gq = rr % a.group;
+      qv[k] = a.q[((size_t)w * a.n_q_heads + kvh * a.group + gq) * D + d];
+    }
+  }
+  const double fq = tid < D / 2 ? a.turn_freq[tid] : 0.0;
+  S st[NST];
+  if (wb < we) {
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k)
+      fetch_group(st[k], db, a, kl, vl, head_groups, wb + k < we ? wb + k : we - 1, we, row_w, lane);
+  }
+  // Stage the queries, pre-scaled by softmax_scale * log2(e), and the rotation
+  // frequencies in turns per position.
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * 256;
+    if (i < RT * 16 * D) smem[(i / D) * QSTRIDE + i % D] = qv[k] * a.q_scale;
+  }
+  if (tid < D / 2) sm_freq[tid] = fq;
+  __syncthreads();
+
   f32x4 o[RT][NDT];
   float m[RT], l[RT];
-  typename F::QOp qop[RT][NC];
   bool rowvis[RT];
+  bool rowmask[RT];   // wave-uniform: some real row of this tile does not see the block
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = -INFINITY;
     l[rt] = 0.0f;
     rowvis[rt] = false;
+    rowmask[rt] = false;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qop[rt][c] = F::zero_q();
   }
   int cur_seg = -1;
 
-  long long gi = begin + wave;
-  F cur, nxt;
-  int2 dcur = make_int2(0, 0), dnxt = make_int2(0, 0);
-  if (gi < end) {
-    dcur = a.groups[gi];
-    const size_t gb = ((size_t)dcur.x + head_groups) * (size_t)(32 * D);
-    cur.load(kl + gb, vl + gb, lane);
-  }
-  for (; gi < end; gi += kWaves) {
-    // Prefetch the wave's next group while this one is computed.
-    const long long gn = gi + kWaves;
-    if (gn < end) {
-      dnxt = a.groups[gn];
-      const size_t gb = ((size_t)dnxt.x + head_groups) * (size_t)(32 * D);
-      nxt.load(kl + gb, vl + gb, lane);
-    }
-    const int seg = dcur.y >> 8;
-    const int nvalid = dcur.y & 255;
-
-    // Entering a new block: rotate each row's query by q_pos(w) - offset(w, block).
+  auto process = [&](const S &sg) __attribute__((always_inline)) {
+    const int seg = sg.desc_y >> 8;
+    const int nvalid = sg.desc_y & 255;
+    // Entering a new block: rotate each row's query by delta = q_pos(w) - offset(w, block).
+    // The angle delta * theta_j is reduced to a fraction of a turn in fp64; the sine and
+    // cosine of that fraction come from the hardware's fp32 units.
     if (seg != cur_seg) {
       cur_seg = seg;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + col;
-        int dl = -1;
-        if (r < nrows) dl = a.delta[(size_t)seg * a.n_workers + (row0 + r) / a.group];
-        rowvis[rt] = dl >= 0;
-        const float *qrow = smem + r * QSTRIDE;
-        const float2 *tr = a.trig + (size_t)(dl < 0 ? 0 : dl) * (D / 2);
+        const int dl = sg.delta[rt];
+        rowvis[rt] = row_ok[rt] && dl >= 0;
+        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
+        const float *qrow = smem + (rt * 16 + col) * QSTRIDE;
+        const double ddl = (double)(dl < 0 ? 0 : dl);
 #pragma unroll
         for (int c = 0; c < NC / 2; ++c) {
           const int j0 = 32 * c + 8 * grp;
           float lo[8], hi[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float2 cs = tr[j0 + e];
+            const double turns = ddl * sm_freq[j0 + e];
+            const float r = (float)(turns - __builtin_rint(turns));
+            const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
             const float x0 = qrow[j0 + e], x1 = qrow[D / 2 + j0 + e];
-            lo[e] = x0 * cs.x - x1 * cs.y;
-            hi[e] = x1 * cs.x + x0 * cs.y;
+            lo[e] = x0 * cs - x1 * sn;
+            hi[e] = x1 * cs + x0 * sn;
           }
-          if (rowvis[rt]) {
-            qop[rt][c] = F::make_q(lo);
-            qop[rt][c + NC / 2] = F::make_q(hi);
-          } else {
-            qop[rt][c] = F::zero_q();
-            qop[rt][c + NC / 2] = F::zero_q();
-          }
+          qop_lds[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
+          qop_lds[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+          // one chunk at a time: keeps the rotation's temporaries from crowding out the
+          // accumulators and the stages in flight
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
     // Scores of the 32 tokens for every row: lane (row col, group grp) gets tokens
-    // 8*grp + 4*hh + r of row rt*16 + col in s[rt][hh][r].
-    f32x4 s[RT][2];
+    // 8*grp + 4*hh + r of row rt*16 + col in sc[rt][hh][r].
+    f32x4 sc[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = cur.score(c, hh, qop[rt][c], acc);
-        s[rt][hh] = acc;
+        for (int c = 0; c < NC; ++c) acc = sg.f.score(c, hh, qop_lds[(rt * NC + c) * 64 + lane], acc);
+        sc[rt][hh] = acc;
       }
 
-    // Online softmax (log2 domain), one row per lane, 8 tokens per lane.
-    typename F::POp pop[RT];
+    // Online softmax in the log2 domain, one row per lane, 8 tokens per lane. At most one
+    // uniform branch for masking and one for rescaling per group, so that the MFMAs of one
+    // row tile can overlap the softmax of the next. Rows past the workgroup's real rows
+    // are never written out, so they need no mask.
+    float v8[RT][8], mx[RT];
+    bool any_mask = nvalid < 32;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) any_mask |= rowmask[rt];
+    if (any_mask) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * grp + e;
+          const float x = sc[rt][e >> 2][e & 3];
+          v8[rt][e] = ((rowvis[rt] || !row_ok[rt]) && u < nvalid) ? x : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[rt][e] = sc[rt][e >> 2][e & 3];
+    }
+    bool grow = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float v8[8];
-      float mx = -INFINITY;
+      float x = v8[rt][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int u = 8 * grp + e;
-        const float x = s[rt][e >> 2][e & 3];
-        v8[e] = (rowvis[rt] && u < nvalid) ? x : -INFINITY;
-        mx = fmaxf(mx, v8[e]);
+      for (int e = 1; e < 8; ++e) x = fmaxf(x, v8[rt][e]);
+      mx[rt] = wave_max_across_groups(x);
+      grow |= mx[rt] > m[rt] + kRescaleLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mnew = fmaxf(m[rt], mx[rt]);
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - (mnew == -INFINITY ? 0.0f : mnew));
+        l[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
+        m[rt] = mnew;
       }
-      mx = wave_max_across_groups(mx);
-      const float mnew = fmaxf(m[rt], mx);
-      const float msafe = mnew == -INFINITY ? 0.0f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[rt] - msafe);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float msafe = m[rt] == -INFINITY ? 0.0f : m[rt];
       float p[8], sum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(v8[e] - msafe);
+        p[e] = __builtin_amdgcn_exp2f(v8[rt][e] - msafe);
         sum += p[e];
       }
-      l[rt] = l[rt] * alpha + sum;
-      m[rt] = mnew;
+      l[rt] += sum;
+      const typename F::POp pop = F::make_p(p);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
-      pop[rt] = F::make_p(p);
+      for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = sg.f.pv(dt, pop, o[rt][dt]);
     }
+  };
 
+  // NST stages per wave: while one group is computed the next NST-1 load. The prefetch is
+  // unconditional (past the end the last group is fetched again, from cache) so that the
+  // wait for a stage never has to assume that no younger loads are outstanding.
+  if (wb < we) {
+    long long gi = wb;
+    for (;;) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = cur.pv(dt, pop[rt], o[rt][dt]);
-
-    cur = nxt;
-    dcur = dnxt;
+      for (int k = 0; k < NST; ++k) {
+        const long long gf = gi + NST - 1;
+        fetch_group(st[(k + NST - 1) % NST], db, a, kl, vl, head_groups, gf < we ? gf : we - 1,
+                    we, row_w, lane);
+        process(st[k]);
+        if (++gi >= we) goto groups_done;
+      }
+    }
   }
+groups_done:
 
-  // ---- combine the four waves (fixed order: (w0 + w2) + (w1 + w3)) ----
+  // ---- combine the four waves: common max, then one LDS pass in which every wave adds
+  // a quarter of the rows' slots in fixed order (w0 + w1) + (w2 + w3) ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
   __syncthreads();  // every wave is done with the staged queries
@@ -433,111 +552,121 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
     }
   }
   __syncthreads();
-  float mrow[RT], lrow[RT];
+  f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + col;
     float mm = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][r]);
-    float ll = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][r];
-      ll += mw == -INFINITY ? 0.0f : sm_l[w][r] * __builtin_amdgcn_exp2f(mw - mm);
-    }
-    mrow[rt] = mm;
-    lrow[rt] = ll;
     const float fac = m[rt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[rt] - mm);
+    if (wave == 0 && grp == 0) {
+      float ll = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= fac;
-  }
-  f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
-  if (wave >= 2) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][r];
+        ll += mw == -INFINITY ? 0.0f : sm_l[w][r] * __builtin_amdgcn_exp2f(mw - mm);
+      }
+      sm_rowm[r] = mm;
+      sm_rowl[r] = ll;
+    }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        buf[(wave - 2) * BUF_F4 + (rt * NDT + dt) * 64 + lane] = o[rt][dt];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        o[rt][dt] += buf[wave * BUF_F4 + (rt * NDT + dt) * 64 + lane];
+    for (int dt = 0; dt < NDT; ++dt) buf[wave * SLOTS + (rt * NDT + dt) * 64 + lane] = o[rt][dt] * fac;
   }
   __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) buf[(rt * NDT + dt) * 64 + lane] = o[rt][dt];
-  }
-  __syncthreads();
-  if (wave != 0) return;
 
   const bool direct = a.n_splits == 1;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + col;
+  for (int sl = tid; sl < SLOTS; sl += 256) {
+    const int rt = sl / (NDT * 64), dt = (sl / 64) % NDT, ln = sl % 64;
+    const int r = rt * 16 + (ln & 15);
     if (r >= nrows) continue;
-    const int rr = row0 + r;
-    const float L = lrow[rt];
+    const f32x4 x = (buf[sl] + buf[SLOTS + sl]) + (buf[2 * SLOTS + sl] + buf[3 * SLOTS + sl]);
+    const float L = sm_rowl[r];
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const float lse2 = L > 0.0f ? mrow[rt] + __log2f(L) : -INFINITY;
+    const int rr = row0 + r;
     float *dst;
     if (direct) {
       const int w = rr / a.group, h = kvh * a.group + rr % a.group;
       dst = a.out + ((size_t)w * a.n_q_heads + h) * D;
-      if (grp == 0 && a.lse) a.lse[(size_t)w * a.n_q_heads + h] = lse2 * 0.69314718055994531f;
+      if (dt == 0 && (ln >> 4) == 0 && a.lse)
+        a.lse[(size_t)w * a.n_q_heads + h] =
+            L > 0.0f ? (sm_rowm[r] + __log2f(L)) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t prow = ((size_t)split * a.n_kv_heads + kvh) * a.rows + rr;
       dst = a.part_o + prow * D;
-      if (grp == 0) a.part_lse[prow] = lse2;
+      if (dt == 0 && (ln >> 4) == 0) a.part_lse[prow] = L > 0.0f ? sm_rowm[r] + __log2f(L) : -INFINITY;
     }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const f32x4 x = (o[rt][dt] + buf[(rt * NDT + dt) * 64 + lane]) * inv;
-      *reinterpret_cast<float4 *>(dst + 16 * dt + 4 * grp) = make_float4(x[0], x[1], x[2], x[3]);
-    }
+    *reinterpret_cast<float4 *>(dst + 16 * dt + 4 * (ln >> 4)) =
+        make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
   }
 }
 
 // ------------------------------------------------------------------------------------
-// lse_merge: one wave per (worker, query head) row.
+// lse_merge: four lanes per (worker, query head, 4 output dims); lane j of the four merges
+// partials j, j+4, ... with all of its loads in flight together, and the four running
+// results are combined with lane exchanges.
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.n_workers * a.n_q_heads) return;
+  constexpr int Q4 = D / 4;
+  constexpr int B = 8;   // partials per lane whose loads are in flight together
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int sub = t & 3;
+  const int item = t >> 2;
+  const bool live = item < a.n_workers * a.n_q_heads * Q4;
+  const int it = live ? item : 0;
+  const int row = it / Q4, q4 = it % Q4;
   const int w = row / a.n_q_heads, h = row % a.n_q_heads;
   const int kvh = h / a.group;
   const int rr = w * a.group + h % a.group;
   const size_t stride = (size_t)a.n_kv_heads * a.rows;
   const size_t base = (size_t)kvh * a.rows + rr;
-  float mm = -INFINITY;
-  for (int p = 0; p < a.n_splits; ++p) mm = fmaxf(mm, a.part_lse[base + p * stride]);
-  float acc[PER];
+  float mm = -INFINITY, tot = 0.0f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = sub; p0 < a.n_splits; p0 += 4 * B) {
+    float lp[B];
+    float4 x[B];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  float tot = 0.0f;
-  for (int p = 0; p < a.n_splits; ++p) {
-    const float lp = a.part_lse[base + p * stride];
-    const float wt = lp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lp - mm);
-    tot += wt;
-    const float *src = a.part_o + (base + p * stride) * D;
+    for (int i = 0; i < B; ++i) {
+      const int p = p0 + 4 * i < a.n_splits ? p0 + 4 * i : 0;
+      lp[i] = a.part_lse[base + p * stride];
+      x[i] = reinterpret_cast<const float4 *>(a.part_o + (base + p * stride) * D)[q4];
+    }
+    float bm = mm;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += wt * src[lane * PER + i];
+    for (int i = 0; i < B; ++i)
+      if (p0 + 4 * i < a.n_splits) bm = fmaxf(bm, lp[i]);
+    if (bm == -INFINITY) continue;
+    const float sc = __builtin_amdgcn_exp2f(mm - bm);
+    tot *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const float wt = (p0 + 4 * i < a.n_splits) ? __builtin_amdgcn_exp2f(lp[i] - bm) : 0.0f;
+      tot += wt;
+      acc += wt * f32x4{x[i].x, x[i].y, x[i].z, x[i].w};
+    }
+    mm = bm;
   }
-  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-  float *dst = a.out + ((size_t)w * a.n_q_heads + h) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[lane * PER + i] = acc[i] * inv;
-  if (lane == 0 && a.lse)
+  for (int off = 1; off < 4; off <<= 1) {
+    const float om = __shfl_xor(mm, off);
+    const float ot = __shfl_xor(tot, off);
+    f32x4 oa;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) oa[k] = __shfl_xor(acc[k], off);
+    const float nm = fmaxf(mm, om);
+    const float fs = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mm - nm);
+    const float fo = om == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(om - nm);
+    tot = tot * fs + ot * fo;
+    acc = acc * fs + oa * fo;
+    mm = nm;
+  }
+  if (!live || sub != 0) return;
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  reinterpret_cast<float4 *>(a.out + ((size_t)w * a.n_q_heads + h) * D)[q4] =
+      make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (q4 == 0 && a.lse)
     a.lse[(size_t)w * a.n_q_heads + h] =
         tot > 0.0f ? (mm + __log2f(tot)) * 0.69314718055994531f : -INFINITY;
 }
@@ -565,17 +694,22 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 template <typename KV, int D>
 static void launch_decode_rt(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s) {
   dim3 block(256);
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 3>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 4>), grid, block, 0, s, a); break;
+  if constexpr (sizeof(KV) == 4) {
+    if (rt == 1) hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, a);
+  } else {
+    switch (rt) {
+      case 1: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 3>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 4>), grid, block, 0, s, a); break;
+    }
   }
 }
 
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
                          hipStream_t s) {
-  const int rows_first = a.rows < kRowsPerBlock ? a.rows : kRowsPerBlock;
+  const int rows_first = a.rows < a.rows_per_block ? a.rows : a.rows_per_block;
   const int rt = (rows_first + 15) / 16;
   dim3 grid(a.n_splits, a.n_kv_heads, row_blocks);
   if (dt == HW_BF16) {
@@ -588,9 +722,10 @@ hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row
   return hipGetLastError();
 }
 
+
 hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s) {
-  const int rows = a.n_workers * a.n_q_heads;
-  dim3 grid((rows + 3) / 4), block(256);
+  const int threads = 4 * a.n_workers * a.n_q_heads * (head_dim / 4);
+  dim3 grid((threads + 255) / 256), block(256);
   if (head_dim == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, block, 0, s, a);
   return hipGetLastError();

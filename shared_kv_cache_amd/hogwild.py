@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_reset_block",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
-           "hw_debug_resolve"]
+           "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed"]
 
 
 class HwConfig(ctypes.Structure):
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_free_pages": (c_int, [c_void_p, P32]),
         "hw_debug_reserve": (c_int, [c_void_p, c_int32, c_int32, P32, P32, P32, c_int32, P32]),
         "hw_debug_resolve": (c_int, [c_void_p, c_int32, P32, P32, c_int32, P32, P32, c_int32, P32, P32]),
+        "hw_debug_kernel_events": (c_int, [c_void_p, c_int32]),
+        "hw_debug_kernel_elapsed": (c_int, [c_void_p, POINTER(c_float), c_int32, P32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -195,6 +197,17 @@ def hw_debug_resolve(ctx, layer: int, n_workers: int, cap_segs: int = 4096,
             "delta": [list(delta[s * n_workers:(s + 1) * n_workers]) for s in range(ns)],
             "n_segs": n_seg.value, "n_groups": n_grp.value, "n_splits": n_split.value,
             "groups": [tuple(groups[4 * i:4 * i + 4]) for i in range(n_grp.value)]}
+
+
+def hw_debug_kernel_events(ctx, capacity: int) -> None:
+    _check(ctx, load_library().hw_debug_kernel_events(ctx, capacity))
+
+
+def hw_debug_kernel_elapsed(ctx, cap: int = 1 << 16):
+    dec = (c_float * cap)()
+    n = c_int32()
+    _check(ctx, load_library().hw_debug_kernel_elapsed(ctx, dec, cap, ctypes.byref(n)))
+    return list(dec[:min(n.value, cap)])
 
 
 # ---------------------------------------------------------------- owner

@@ -69,7 +69,7 @@ def test_workspace_size_formula(ctx):
     al = lambda x: (x + 255) // 256 * 256
     max_groups = 16 * (64 // 32)
     rows = 4 * 4
-    expect = al(max_pos * half * 8)
+    expect = al(max_pos * half * 8) + al(half * 8)
     expect += al(al(16 * 4 * 4) + al(max_groups * 8))
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
