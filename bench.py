@@ -7,9 +7,9 @@ seeded synthetic tensors already resident in HBM when the timed region starts.
 
 Prints ONE JSON line: worker-steps/s (value), the step's ideal-bytes GB/s,
 a roofline object for the dominant kernel (concurrent_decode: algorithmic
-bytes per launch / its average launch duration from HIP events recorded on the
-launch stream inside the timed region) and the fp64 oracle's CPU rate on a
-bounded sample of the same workload.
+bytes per launch / its average duration, from start/stop HIP events that the
+kernel's own dispatch records on its stream during a timed pass) and the fp64
+oracle's CPU rate on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -165,7 +165,7 @@ def main() -> int:
     t_tok1 = tokens_now()
     log(f"timed: {args.steps} steps in {ms_total:.3f} ms")
 
-    # Timed region 2: the same steps with HIP events around each kernel launch.
+    # Timed region 2: the same steps, the decode kernels recording start/stop events.
     H.hw_debug_kernel_events(cache.ctx, args.steps * L)
     torch.cuda.synchronize()
     for _ in range(args.steps):

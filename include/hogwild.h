@@ -16,11 +16,15 @@
  *     ID), s2.2 (rotate q by the block offset; rotation is an isometry).
  *
  * Conventions fixed here (the pages leave them open):
- *   RoPE   pairs (j, j + d/2) rotated by pos * theta^(-2j/d). The fp32 cos/sin of every
- *          position p < max_position is computed once on the host in fp64 with libm
- *          cos/sin of (double)p * pow(theta, -(2.0*j)/d), rounded once to fp32.
+ *   RoPE   pairs (j, j + d/2) rotated by pos * theta^(-2j/d). For stored keys, the fp32
+ *          cos/sin of every position p < max_position is computed once on the host in fp64
+ *          with libm cos/sin of (double)p * pow(theta, -(2.0*j)/d), rounded once to fp32.
  *   Query  q[w][h] is fp32 and unrotated. Row (w, h) reads KV head h / (Hq / Hkv).
  *          Score = (R(delta) q) . k_stored * softmax_scale, delta = q_pos - block offset.
+ *          The decode kernel forms delta * theta_j / (2 pi) in fp64, reduces it to a fraction
+ *          of a turn and takes the hardware's fp32 sine and cosine of that fraction.
+ *          The rotated query and the softmax probabilities enter the matrix cores as bf16
+ *          operands for bf16 pools (fp32 for fp32 pools); accumulation is fp32.
  *   Output out[w][h][:] fp32 and lse[w][h] = ln(sum_t exp(score_t)) fp32.
  *
  * Threading and streams: a context is not thread-safe. Use ONE stream per context for

@@ -40,9 +40,10 @@ hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *d
                            int32_t cap_groups, int32_t *n_groups, int32_t *n_splits);
 
 /* ---- profiling hooks (these two do call HIP) ---------------------------------------------
- * With capacity > 0, each following hw_concurrent_decode records a HIP event pair on its
- * stream around its concurrent_decode kernel (not the split merge that follows it), for up to
- * `capacity` calls; capacity 0 stops recording and frees the events. Errors: HW_ERR_HIP. */
+ * With capacity > 0, each following hw_concurrent_decode has its concurrent_decode kernel
+ * (not the split merge that follows it) record a start and a stop HIP event with its own
+ * dispatch, for up to `capacity` calls; capacity 0 stops recording and frees the events.
+ * Errors: HW_ERR_HIP. */
 hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity);
 
 /* Wait for the recorded events and write, per recorded call i < cap, decode_ms[i]: the

@@ -659,18 +659,12 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   const int32_t row_blocks = row_blocks_for(ctx, n);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
   hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
-  if (prof) {
-    hipError_t e = hipEventRecord(ev[0], s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord(profile)");
-  }
-  hw_status st = post_launch(ctx, hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s),
+  hw_status st = post_launch(ctx,
+                             hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s,
+                                               prof ? ev[0] : nullptr, prof ? ev[1] : nullptr),
                              "concurrent_decode", s);
   if (st != HW_OK) return st;
-  if (prof) {
-    hipError_t e = hipEventRecord(ev[1], s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord(profile)");
-    ctx->prof_count++;
-  }
+  if (prof) ctx->prof_count++;
   if (splits > 1) {
     hw::MergeArgs m{};
     m.part_o = a.part_o;

@@ -17,6 +17,7 @@
 // softmax needs only two cross-lane exchanges per 32 tokens. The pool layouts (hogwild.h)
 // put each lane's 16-byte operand at lane * 16 of a 1 KiB run, so every load is coalesced
 // and lands in operand layout with no LDS staging.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -691,37 +692,39 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
   return hipGetLastError();
 }
 
+// Launched with hipExtLaunchKernelGGL so that optional start/stop events are recorded by
+// the kernel's own dispatch (null events: a plain launch).
 template <typename KV, int D>
-static void launch_decode_rt(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s) {
+static void launch_decode_rt(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
+                             hipEvent_t e1) {
   dim3 block(256);
   if constexpr (sizeof(KV) == 4) {
-    if (rt == 1) hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, a);
+    if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, e0, e1, 0, a);
   } else {
     switch (rt) {
-      case 1: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 3>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((concurrent_decode_kernel<KV, D, 4>), grid, block, 0, s, a); break;
+      case 1: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, e0, e1, 0, a); break;
+      case 2: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, e0, e1, 0, a); break;
+      case 3: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 3>), grid, block, 0, s, e0, e1, 0, a); break;
+      default: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 4>), grid, block, 0, s, e0, e1, 0, a); break;
     }
   }
 }
 
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int rows_first = a.rows < a.rows_per_block ? a.rows : a.rows_per_block;
   const int rt = (rows_first + 15) / 16;
   dim3 grid(a.n_splits, a.n_kv_heads, row_blocks);
   if (dt == HW_BF16) {
-    if (head_dim == 128) launch_decode_rt<__bf16, 128>(rt, a, grid, s);
-    else launch_decode_rt<__bf16, 64>(rt, a, grid, s);
+    if (head_dim == 128) launch_decode_rt<__bf16, 128>(rt, a, grid, s, ev_start, ev_stop);
+    else launch_decode_rt<__bf16, 64>(rt, a, grid, s, ev_start, ev_stop);
   } else {
-    if (head_dim == 128) launch_decode_rt<float, 128>(rt, a, grid, s);
-    else launch_decode_rt<float, 64>(rt, a, grid, s);
+    if (head_dim == 128) launch_decode_rt<float, 128>(rt, a, grid, s, ev_start, ev_stop);
+    else launch_decode_rt<float, 64>(rt, a, grid, s, ev_start, ev_stop);
   }
   return hipGetLastError();
 }
-
 
 hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s) {
   const int threads = 4 * a.n_workers * a.n_q_heads * (head_dim / 4);
