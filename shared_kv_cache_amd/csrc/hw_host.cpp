@@ -155,6 +155,8 @@ hw_status check_config(const hw_config *g, std::string &m) {
   if (g->max_blocks <= 0 || g->max_blocks > (1 << 22)) return m = "max_blocks out of range", HW_ERR_INVALID_ARG;
   if (g->max_workers <= 0 || g->max_workers > 1024) return m = "max_workers out of range", HW_ERR_INVALID_ARG;
   if (g->max_position <= 0) return m = "max_position must be > 0", HW_ERR_INVALID_ARG;
+  if ((int64_t)g->max_workers * (g->n_q_heads / g->n_kv_heads) >= (1 << 22))
+    return m = "max_workers * (n_q_heads / n_kv_heads) must be below 2^22", HW_ERR_INVALID_ARG;
   if (g->max_splits < 0 || g->max_splits > 65535) return m = "max_splits out of range", HW_ERR_INVALID_ARG;
   if (g->kv_dtype != HW_BF16 && g->kv_dtype != HW_F32) return m = "unknown kv_dtype", HW_ERR_INVALID_ARG;
   if (!(g->rope_theta > 1.0) || !std::isfinite(g->rope_theta)) return m = "rope_theta must be > 1", HW_ERR_INVALID_ARG;
@@ -263,8 +265,8 @@ int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
 }
 
 int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
-  if (c->split_override > 0) return std::min(c->split_override, c->cfg.max_splits);
-  return auto_splits(c, n_groups, n_workers);
+  return c->split_override > 0 ? std::min(c->split_override, c->cfg.max_splits)
+                               : auto_splits(c, n_groups, n_workers);
 }
 
 // Signature of everything a resolution depends on; equal signatures => equal tables.
@@ -655,6 +657,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.n_splits = splits;
   a.page_groups = g.page_size / hw::kTokGroup;
   a.rows_per_block = hw::rows_per_block(g.kv_dtype);
+  a.inv_group = 1.0f / (float)group;
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
   const int32_t row_blocks = row_blocks_for(ctx, n);
   const bool prof = ctx->prof_count < ctx->prof_capacity;

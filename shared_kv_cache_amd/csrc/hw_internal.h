@@ -10,9 +10,8 @@
 namespace hw {
 
 constexpr int kTokGroup = 32;          // tokens per pool group (one MFMA K/V tile)
-constexpr int kWaves = 4;              // waves per decode workgroup
 constexpr int kRowsPerBlock = 64;      // stacked (worker, query head) rows per decode workgroup
-constexpr int kRowsPerBlockF32 = 32;   // the same for fp32 pools (their operands are twice as wide)
+constexpr int kRowsPerBlockF32 = 16;   // the same for fp32 pools (exact-check path; wider operands)
 
 inline int rows_per_block(hw_dtype dt) { return dt == HW_F32 ? kRowsPerBlockF32 : kRowsPerBlock; }
 constexpr int kMaxRunsPerLaunch = 64;  // append runs carried in one launch's arguments
@@ -58,6 +57,7 @@ struct DecodeArgs {
   int32_t n_splits;
   int32_t page_groups;
   int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)
+  float inv_group;         // 1 / group (rows < 2^22, so the worker of a row is exact in fp32)
   float q_scale;           // softmax_scale * log2(e)
 };
 

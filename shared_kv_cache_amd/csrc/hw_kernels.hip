@@ -150,6 +150,18 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
 // ------------------------------------------------------------------------------------
 
 // Per-dtype pieces: the operand fragments a lane holds and the two matrix products.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte load, with the non-temporal (streaming) hint when NT.
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const __bf16 *p) {
+  if constexpr (NT) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+
 template <typename KV, int D>
 struct Frag;
 
@@ -162,15 +174,18 @@ struct Frag<__bf16, D> {
   using QOp = bf16x8;                 // rotated query chunk
   using POp = bf16x8;                 // probabilities of 8 tokens
 
+  // NT: the group is read by one wave only, so its loads carry the streaming hint and do
+  // not evict the small tables that every launch reads first (descriptors, offsets,
+  // queries). Groups read by two waves keep ordinary loads: the second read hits L2.
+  template <bool NT>
   __device__ __forceinline__ void load(const __bf16 *kg, const __bf16 *vg, int lane) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        k[c][hh] = *reinterpret_cast<const uint4 *>(kg + ((c * 2 + hh) * 64 + lane) * 8);
+        k[c][hh] = ld16<NT>(kg + ((c * 2 + hh) * 64 + lane) * 8);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      v[dt] = *reinterpret_cast<const uint4 *>(vg + (dt * 64 + lane) * 8);
+    for (int dt = 0; dt < NDT; ++dt) v[dt] = ld16<NT>(vg + (dt * 64 + lane) * 8);
   }
   static __device__ __forceinline__ QOp make_q(const float *x) {
     QOp r;
@@ -208,6 +223,7 @@ struct Frag<float, D> {
   using QOp = F8;
   using POp = F8;
 
+  template <bool NT>
   __device__ __forceinline__ void load(const float *kg, const float *vg, int lane) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -273,67 +289,67 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 // stale max and stay below 2^8, well inside bf16 and fp32 range.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Per-wave pipeline state: one 32-token group's operands, its descriptor (wave-uniform) and
-// the query offsets of the lane's rows for the group's block.
-template <typename KV, int D, int RT>
+// Group descriptors are wave-uniform: they are read through the scalar cache (constant
+// address space), whose loads are counted apart from the vector loads of K and V.
+typedef __attribute__((address_space(4))) const int ConstInt;
+__device__ __forceinline__ int2 load_desc(const int2 *groups, long long i) {
+  const ConstInt *p = (const ConstInt *)groups;
+  return make_int2(p[2 * i], p[2 * i + 1]);
+}
+
+// Per-wave pipeline state: one 32-token group's operands and its descriptor (wave-uniform).
+template <typename KV, int D>
 struct Stage {
   Frag<KV, D> f;
   int desc_x, desc_y;
-  int delta[RT];
 };
 
-// A wave's group descriptors, 64 at a time: lane j holds descriptor base + j. One vector
-// load replaces a dependent scalar load per group.
-struct DescBatch {
-  long long base;
-  int x, y;
-};
-
-__device__ __forceinline__ void load_desc_batch(DescBatch &db, const int2 *groups, long long base,
-                                                long long end, int lane) {
-  db.base = base;
-  int2 d = make_int2(0, 0);
-  if (base + lane < end) d = groups[base + lane];
-  db.x = d.x;
-  db.y = d.y;
+// Issue one group's K and V loads (each group is read by one wave: streaming hint).
+template <typename KV, int D>
+__device__ __forceinline__ void fetch_group(Stage<KV, D> &st, int2 desc, const KV *kl,
+                                            const KV *vl, size_t head_groups, int lane) {
+  st.desc_x = desc.x;
+  st.desc_y = desc.y;
+  const size_t gb = ((size_t)desc.x + head_groups) * (size_t)(32 * D);
+  st.f.template load<true>(kl + gb, vl + gb, lane);
 }
 
-template <typename KV, int D, int RT>
-__device__ __forceinline__ void fetch_group(Stage<KV, D, RT> &st, DescBatch &db,
-                                            const DecodeArgs &a, const KV *kl, const KV *vl,
-                                            size_t head_groups, long long g, long long we,
-                                            const int *row_w, int lane) {
-  if (g - db.base >= 64) load_desc_batch(db, a.groups, db.base + 64, we, lane);
-  const int j = (int)(g - db.base);
-  st.desc_x = __builtin_amdgcn_readlane(db.x, j);
-  st.desc_y = __builtin_amdgcn_readlane(db.y, j);
-  const int seg = st.desc_y >> 8;
+// Issue the loads of the query offsets of the lane's rows for the block of segment seg.
+template <int RTW>
+__device__ __forceinline__ void fetch_delta(int (&dl)[RTW], int seg, const DecodeArgs &a,
+                                            const int *row_w) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) st.delta[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
-  const size_t gb = ((size_t)st.desc_x + head_groups) * (size_t)(32 * D);
-  st.f.load(kl + gb, vl + gb, lane);
+  for (int rt = 0; rt < RTW; ++rt) dl[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
 }
 
 __device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-template <typename KV, int D, int RT>
-__global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a) {
+// One workgroup = one (split, KV head, block of up to 16 * RTW rows), NW waves. Every wave
+// holds all RTW row tiles and takes a contiguous run of the workgroup's token groups, so
+// each group is read from HBM by exactly one wave. NST register stages per wave: with one,
+// the group's loads are issued and then it is computed, the other wave on the SIMD (NW = 8)
+// computing meanwhile; with two (NW = 4, one wave per SIMD, for wide row tiles whose
+// accumulators fill the registers of two waves), the next group is in flight while one is
+// computed.
+template <typename KV, int D, int RTW, int NW, int NST>
+__global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
+  static_assert(NST == 1 || NST == 2, "one or two stages");
   using F = Frag<KV, D>;
-  using S = Stage<KV, D, RT>;
+  using S = Stage<KV, D>;
   using QOp = typename F::QOp;
   constexpr int NC = F::NC, NDT = F::NDT;
-  // Pipeline stages per wave (NST - 1 groups in flight), as many as the registers allow.
-  constexpr int NST = (RT <= 2 && sizeof(KV) == 2) ? 3 : 2;
+  constexpr int RT = RTW;                          // row tiles of the workgroup
+  constexpr int NT = NW * 64;
   constexpr int QSTRIDE = D + 4;                   // padded q row (LDS bank spread)
   constexpr int Q_FLOATS = RT * 16 * QSTRIDE;
-  constexpr int QOP_FLOATS = kWaves * RT * NC * 64 * (int)(sizeof(QOp) / 4);
-  constexpr int SLOTS = RT * NDT * 64;             // one wave's O^T, f32x4 slots in lane order
-  constexpr int M_FLOATS = kWaves * SLOTS * 4;
+  constexpr int QOP_FLOATS = NW * RTW * NC * 64 * (int)(sizeof(QOp) / 4);
+  constexpr int SLOTS = RTW * NDT * 64;            // one wave's O^T, f32x4 slots in lane order
+  constexpr int M_FLOATS = NW * SLOTS * 4;
   constexpr int SMEM = Q_FLOATS + QOP_FLOATS > M_FLOATS ? Q_FLOATS + QOP_FLOATS : M_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
   __shared__ double sm_freq[D / 2];
-  __shared__ float sm_m[kWaves][64];
-  __shared__ float sm_l[kWaves][64];
+  __shared__ float sm_m[NW][16 * RTW];
+  __shared__ float sm_l[NW][16 * RTW];
   __shared__ float sm_rowm[64], sm_rowl[64];
 
   const int tid = threadIdx.x;
@@ -344,66 +360,82 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
   const int row0 = blockIdx.z * a.rows_per_block;
   const int nrows = min(a.rows_per_block, a.rows - row0);
   // Rotated query operands of this wave, in lane order: [rt][chunk][lane].
-  QOp *qop_lds = reinterpret_cast<QOp *>(smem + Q_FLOATS) + (size_t)wave * RT * NC * 64;
+  QOp *qop_lds = reinterpret_cast<QOp *>(smem + Q_FLOATS) + (size_t)wave * RTW * NC * 64;
 
-  // This workgroup's range of token groups, cut into one contiguous range per wave.
+  // This workgroup's token groups [begin, end); this wave's contiguous run of them.
   const long long begin = (long long)split * a.n_groups / a.n_splits;
   const long long end = (long long)(split + 1) * a.n_groups / a.n_splits;
-  const long long wb = begin + (end - begin) * wave / kWaves;
-  const long long we = begin + (end - begin) * (wave + 1) / kWaves;
+  const long long wfirst = begin + (end - begin) * wave / NW;
+  const long long wcount = begin + (end - begin) * (wave + 1) / NW - wfirst;
   const KV *kl = static_cast<const KV *>(a.k_layer);
   const KV *vl = static_cast<const KV *>(a.v_layer);
   const size_t head_groups = (size_t)kvh * a.page_groups;
 
-  int row_w[RT];
-  bool row_ok[RT];
+  // Worker of stacked row rr = rr / group, computed as floor((rr + 0.5) * (1 / group)) in
+  // fp32: exact while rr < 2^22, as the error of the product stays below 0.5 / group.
+  auto worker_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
+  // The lane's rows: row rt * 16 + col of the workgroup's block.
+  int row_w[RTW];
+  bool row_ok[RTW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RTW; ++rt) {
     const int r = rt * 16 + col;
     row_ok[rt] = r < nrows;
-    row_w[rt] = row_ok[rt] ? (row0 + r) / a.group : 0;
+    row_w[rt] = row_ok[rt] ? worker_of(row0 + r) : 0;
   }
 
-  // Issue order: descriptors, raw queries, then the first groups' K/V, so that waiting for
-  // the older loads leaves the K/V loads in flight.
-  DescBatch db;
-  load_desc_batch(db, a.groups, wb, we, lane);
-  constexpr int QPT = (RT * 16 * D + 255) / 256;   // query values per thread
-  float qv[QPT];
+  // Prologue, ordered for latency: the first descriptors (scalar), the raw queries and
+  // rotation frequencies, then the first groups' offsets and K/V; only then the wait for
+  // the queries, which leaves those loads in flight. A fetch with nothing to fetch (no
+  // group for this wave, or past the end of its run) still issues its loads, from
+  // descriptor (0, 0): page 0 of the head and the first row of the offset table, both
+  // always allocated; the data goes unused. Loads issued unconditionally keep the waits
+  // for each stage exact.
+  const long long wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);
+  int2 desc = make_int2(0, 0), next = make_int2(0, 0), next2 = make_int2(0, 0);
+  if (wcount > 0) desc = load_desc(a.groups, wfirst);   // only groups of this wave's run
+  if (wcount > 1) next = load_desc(a.groups, wfirst + 1);
+  constexpr int QV4 = (RT * 16 * D / 4 + NT - 1) / NT;   // float4 of queries per thread
+  float4 qv[QV4];
 #pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + k * 256;
-    const int r = i / D, d = i % D;
-    qv[k] = 0.0f;
-    if (i < RT * 16 * D && r < nrows) {
+  for (int k = 0; k < QV4; ++k) {
+    const int i = tid + k * NT;                      // float4 index in [RT*16][D/4]
+    const int r = i / (D / 4), d4 = i % (D / 4);
+    qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < RT * 16 * D / 4 && r < nrows) {
       const int rr = row0 + r;
-      const int w = rr / a.group, gq = rr % a.group;
-      qv[k] = a.q[((size_t)w * a.n_q_heads + kvh * a.group + gq) * D + d];
+      const int w = worker_of(rr), gq = rr - w * a.group;
+      qv[k] = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.n_q_heads + kvh * a.group + gq) * D)[d4];
     }
   }
   const double fq = tid < D / 2 ? a.turn_freq[tid] : 0.0;
-  S st[NST];
-  if (wb < we) {
-#pragma unroll
-    for (int k = 0; k < NST - 1; ++k)
-      fetch_group(st[k], db, a, kl, vl, head_groups, wb + k < we ? wb + k : we - 1, we, row_w, lane);
-  }
+  S st, st2;
+  int dl_cur[RTW], dl_next[RTW];
+  fetch_delta(dl_cur, desc.y >> 8, a, row_w);
+  fetch_group(st, desc, kl, vl, head_groups, lane);
+  fetch_delta(dl_next, next.y >> 8, a, row_w);
+  if constexpr (NST == 2) fetch_group(st2, next, kl, vl, head_groups, lane);
+  if (wcount > 2) next2 = load_desc(a.groups, wfirst + 2);
   // Stage the queries, pre-scaled by softmax_scale * log2(e), and the rotation
   // frequencies in turns per position.
 #pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + k * 256;
-    if (i < RT * 16 * D) smem[(i / D) * QSTRIDE + i % D] = qv[k] * a.q_scale;
+  for (int k = 0; k < QV4; ++k) {
+    const int i = tid + k * NT;
+    if (i < RT * 16 * D / 4) {
+      const float4 x = qv[k];
+      *reinterpret_cast<float4 *>(smem + (i / (D / 4)) * QSTRIDE + (i % (D / 4)) * 4) =
+          make_float4(x.x * a.q_scale, x.y * a.q_scale, x.z * a.q_scale, x.w * a.q_scale);
+    }
   }
   if (tid < D / 2) sm_freq[tid] = fq;
   __syncthreads();
 
-  f32x4 o[RT][NDT];
-  float m[RT], l[RT];
-  bool rowvis[RT];
-  bool rowmask[RT];   // wave-uniform: some real row of this tile does not see the block
+  f32x4 o[RTW][NDT];
+  float m[RTW], l[RTW];
+  bool rowvis[RTW];
+  bool rowmask[RTW];   // wave-uniform: some real row of this tile does not see the block
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RTW; ++rt) {
     m[rt] = -INFINITY;
     l[rt] = 0.0f;
     rowvis[rt] = false;
@@ -413,19 +445,23 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
   }
   int cur_seg = -1;
 
-  auto process = [&](const S &sg) __attribute__((always_inline)) {
+  auto process = [&](const S &sg, const int (&delta)[RTW]) __attribute__((always_inline)) {
     const int seg = sg.desc_y >> 8;
     const int nvalid = sg.desc_y & 255;
     // Entering a new block: rotate each row's query by delta = q_pos(w) - offset(w, block).
     // The angle delta * theta_j is reduced to a fraction of a turn in fp64; the sine and
     // cosine of that fraction come from the hardware's fp32 units.
+    // Visibility of the block for the lane's rows.
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      rowvis[rt] = row_ok[rt] && delta[rt] >= 0;
+      rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && delta[rt] < 0) != 0;
+    }
     if (seg != cur_seg) {
       cur_seg = seg;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int dl = sg.delta[rt];
-        rowvis[rt] = row_ok[rt] && dl >= 0;
-        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
+      for (int rt = 0; rt < RTW; ++rt) {
+        const int dl = delta[rt];
         const float *qrow = smem + (rt * 16 + col) * QSTRIDE;
         const double ddl = (double)(dl < 0 ? 0 : dl);
 #pragma unroll
@@ -444,17 +480,17 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
           qop_lds[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
           qop_lds[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
           // one chunk at a time: keeps the rotation's temporaries from crowding out the
-          // accumulators and the stages in flight
+          // accumulators and the stage in flight
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
     // Scores of the 32 tokens for every row: lane (row col, group grp) gets tokens
-    // 8*grp + 4*hh + r of row rt*16 + col in sc[rt][hh][r].
-    f32x4 sc[RT][2];
+    // 8*grp + 4*hh + r of row tile rt in sc[rt][hh][r].
+    f32x4 sc[RTW][2];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -463,17 +499,16 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
         sc[rt][hh] = acc;
       }
 
-    // Online softmax in the log2 domain, one row per lane, 8 tokens per lane. At most one
-    // uniform branch for masking and one for rescaling per group, so that the MFMAs of one
-    // row tile can overlap the softmax of the next. Rows past the workgroup's real rows
-    // are never written out, so they need no mask.
-    float v8[RT][8], mx[RT];
+    // Online softmax in the log2 domain, one row per lane, 8 tokens per lane, with at most
+    // one uniform branch for masking and one for rescaling. Rows past the workgroup's real
+    // rows are never written out, so they need no mask.
+    float v8[RTW][8], mx[RTW];
     bool any_mask = nvalid < 32;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) any_mask |= rowmask[rt];
+    for (int rt = 0; rt < RTW; ++rt) any_mask |= rowmask[rt];
     if (any_mask) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * grp + e;
@@ -482,13 +517,13 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
         }
     } else {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) v8[rt][e] = sc[rt][e >> 2][e & 3];
     }
     bool grow = false;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       float x = v8[rt][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) x = fmaxf(x, v8[rt][e]);
@@ -497,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RTW; ++rt) {
         const float mnew = fmaxf(m[rt], mx[rt]);
         const float alpha = __builtin_amdgcn_exp2f(m[rt] - (mnew == -INFINITY ? 0.0f : mnew));
         l[rt] *= alpha;
@@ -507,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       const float msafe = m[rt] == -INFINITY ? 0.0f : m[rt];
       float p[8], sum = 0.0f;
 #pragma unroll
@@ -522,32 +557,44 @@ __global__ __launch_bounds__(256, 1) void concurrent_decode_kernel(DecodeArgs a)
     }
   };
 
-  // NST stages per wave: while one group is computed the next NST-1 load. The prefetch is
-  // unconditional (past the end the last group is fetched again, from cache) so that the
-  // wait for a stage never has to assume that no younger loads are outstanding.
-  if (wb < we) {
-    long long gi = wb;
-    for (;;) {
+  if constexpr (NST == 1) {
+    // Group i: its descriptor and offsets came with group i-1; group i+1's descriptor is
+    // in and group i+2's on its way.
+    for (long long i = 0; i < wcount; ++i) {
+      if (i > 0) {
+        desc = next;
+        next = next2;
 #pragma unroll
-      for (int k = 0; k < NST; ++k) {
-        const long long gf = gi + NST - 1;
-        fetch_group(st[(k + NST - 1) % NST], db, a, kl, vl, head_groups, gf < we ? gf : we - 1,
-                    we, row_w, lane);
-        process(st[k]);
-        if (++gi >= we) goto groups_done;
+        for (int rt = 0; rt < RTW; ++rt) dl_cur[rt] = dl_next[rt];
+        fetch_group(st, desc, kl, vl, head_groups, lane);
+        fetch_delta(dl_next, next.y >> 8, a, row_w);
+        next2 = load_desc(a.groups, min(wfirst + i + 2, wlast));
       }
+      process(st, dl_cur);
+    }
+  } else {
+    // Two stages, groups i (st) and i+1 (st2) in flight; each stage is refilled with the
+    // group two ahead (or the dummy group) as soon as it has been computed.
+    for (long long i = 0; i < wcount; i += 2) {
+      const int2 da = i + 2 < wcount ? load_desc(a.groups, wfirst + i + 2) : make_int2(0, 0);
+      const int2 db = i + 3 < wcount ? load_desc(a.groups, wfirst + i + 3) : make_int2(0, 0);
+      process(st, dl_cur);
+      fetch_delta(dl_cur, da.y >> 8, a, row_w);
+      fetch_group(st, da, kl, vl, head_groups, lane);
+      if (i + 1 < wcount) process(st2, dl_next);
+      fetch_delta(dl_next, db.y >> 8, a, row_w);
+      fetch_group(st2, db, kl, vl, head_groups, lane);
     }
   }
-groups_done:
 
-  // ---- combine the four waves: common max, then one LDS pass in which every wave adds
-  // a quarter of the rows' slots in fixed order (w0 + w1) + (w2 + w3) ----
+  // ---- combine the waves: common max, then one LDS pass in which every slot is summed
+  // over the waves in a fixed order ----
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
+  for (int rt = 0; rt < RTW; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
   __syncthreads();  // every wave is done with the staged queries
   if (grp == 0) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       sm_m[wave][rt * 16 + col] = m[rt];
       sm_l[wave][rt * 16 + col] = l[rt];
     }
@@ -555,18 +602,18 @@ groups_done:
   __syncthreads();
   f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RTW; ++rt) {
     const int r = rt * 16 + col;
     float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][r]);
+    for (int t = 0; t < NW; ++t) mm = fmaxf(mm, sm_m[t][r]);
     const float fac = m[rt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[rt] - mm);
     if (wave == 0 && grp == 0) {
       float ll = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_m[w][r];
-        ll += mw == -INFINITY ? 0.0f : sm_l[w][r] * __builtin_amdgcn_exp2f(mw - mm);
+      for (int t = 0; t < NW; ++t) {
+        const float mw = sm_m[t][r];
+        ll += mw == -INFINITY ? 0.0f : sm_l[t][r] * __builtin_amdgcn_exp2f(mw - mm);
       }
       sm_rowm[r] = mm;
       sm_rowl[r] = ll;
@@ -577,17 +624,19 @@ groups_done:
   __syncthreads();
 
   const bool direct = a.n_splits == 1;
-  for (int sl = tid; sl < SLOTS; sl += 256) {
-    const int rt = sl / (NDT * 64), dt = (sl / 64) % NDT, ln = sl % 64;
+  for (int q = tid; q < SLOTS; q += NT) {
+    const int rt = q / (NDT * 64), dt = (q / 64) % NDT, ln = q % 64;
     const int r = rt * 16 + (ln & 15);
     if (r >= nrows) continue;
-    const f32x4 x = (buf[sl] + buf[SLOTS + sl]) + (buf[2 * SLOTS + sl] + buf[3 * SLOTS + sl]);
+    f32x4 x = buf[q];
+#pragma unroll
+    for (int t = 1; t < NW; ++t) x += buf[t * SLOTS + q];
     const float L = sm_rowl[r];
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int rr = row0 + r;
     float *dst;
     if (direct) {
-      const int w = rr / a.group, h = kvh * a.group + rr % a.group;
+      const int w = worker_of(rr), h = kvh * a.group + rr - w * a.group;
       dst = a.out + ((size_t)w * a.n_q_heads + h) * D;
       if (dt == 0 && (ln >> 4) == 0 && a.lse)
         a.lse[(size_t)w * a.n_q_heads + h] =
@@ -693,22 +742,16 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 }
 
 // Launched with hipExtLaunchKernelGGL so that optional start/stop events are recorded by
-// the kernel's own dispatch (null events: a plain launch).
-template <typename KV, int D>
-static void launch_decode_rt(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
-                             hipEvent_t e1) {
-  dim3 block(256);
-  if constexpr (sizeof(KV) == 4) {
-    if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, e0, e1, 0, a);
-    else hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, e0, e1, 0, a);
-  } else {
-    switch (rt) {
-      case 1: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 1>), grid, block, 0, s, e0, e1, 0, a); break;
-      case 2: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 2>), grid, block, 0, s, e0, e1, 0, a); break;
-      case 3: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 3>), grid, block, 0, s, e0, e1, 0, a); break;
-      default: hipExtLaunchKernelGGL((concurrent_decode_kernel<KV, D, 4>), grid, block, 0, s, e0, e1, 0, a); break;
-    }
-  }
+// the kernel's own dispatch (null events: a plain launch). bf16 pools: up to 32 rows per
+// workgroup run on 8 single-stage waves; 33..64 rows on 4 two-stage waves.
+template <int D>
+static void launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
+  const dim3 b8(8 * 64), b4(4 * 64);
+  if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2>), grid, b4, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2>), grid, b4, 0, s, e0, e1, 0, a);
 }
 
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
@@ -716,12 +759,15 @@ hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row
   const int rows_first = a.rows < a.rows_per_block ? a.rows : a.rows_per_block;
   const int rt = (rows_first + 15) / 16;
   dim3 grid(a.n_splits, a.n_kv_heads, row_blocks);
+  dim3 block(8 * 64);
   if (dt == HW_BF16) {
-    if (head_dim == 128) launch_decode_rt<__bf16, 128>(rt, a, grid, s, ev_start, ev_stop);
-    else launch_decode_rt<__bf16, 64>(rt, a, grid, s, ev_start, ev_stop);
-  } else {
-    if (head_dim == 128) launch_decode_rt<float, 128>(rt, a, grid, s, ev_start, ev_stop);
-    else launch_decode_rt<float, 64>(rt, a, grid, s, ev_start, ev_stop);
+    if (head_dim == 128) launch_decode_bf16<128>(rt, a, grid, s, ev_start, ev_stop);
+    else launch_decode_bf16<64>(rt, a, grid, s, ev_start, ev_stop);
+  } else {   // fp32 pools: one 16-row tile per workgroup
+    if (head_dim == 128)
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1>), grid, block, 0, s, ev_start, ev_stop, 0, a);
   }
   return hipGetLastError();
 }
