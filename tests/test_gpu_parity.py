@@ -184,6 +184,42 @@ def test_many_rows_multiple_row_blocks_and_empty_view():
     cache.close()
 
 
+_VARIANT_LENGTHS = [33, 1, 64, 65, 7, 0, 31, 32]
+
+
+def _variant_workload(head_dim, n_workers, group):
+    """bf16 workload with n_workers * group rows per KV head: a ragged 300-token history and
+    ragged in-progress blocks (one of them empty), 32-token pages."""
+    base = W.make("tiny_fp32")
+    inprog = list(range(1, n_workers + 1))
+    lengths = {0: 300}
+    lengths.update({b: _VARIANT_LENGTHS[(b - 1) % len(_VARIANT_LENGTHS)] for b in inprog})
+    owners = {0: -1}
+    owners.update({b: b - 1 for b in inprog})
+    pages = sum(-(-n // 32) for n in lengths.values()) + 4
+    return W.Workload(**{**base.__dict__, "name": f"d{head_dim}_rows{n_workers * group}",
+                         "n_workers": n_workers, "n_q_heads": 2 * group, "n_kv_heads": 2,
+                         "head_dim": head_dim, "kv_dtype": "bf16", "value_scale": 1.0,
+                         "inprogress": inprog, "lengths": lengths, "owners": owners,
+                         "n_pages": pages, "max_position": 2048})
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("n_workers,group", [(2, 8), (4, 8), (5, 8), (8, 8), (3, 5)])
+def test_every_bf16_kernel_variant(head_dim, n_workers, group):
+    # 16, 32, 40, 64 and 15 rows per KV head: one to four 16-row tiles, i.e. the 8-wave
+    # single-stage kernels and the 4-wave two-stage kernels, each under automatic and
+    # forced KV partitions.
+    wl = _variant_workload(head_dim, n_workers, group)
+    cache = make_cache(wl, max_blocks=n_workers + 2)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    for splits in (0, 1, 3):
+        H.hw_set_split(cache.ctx, splits)
+        _check_layer(cache, wl, 0)
+    cache.close()
+
+
 def test_errors_leave_gpu_state_unchanged():
     wl = W.make("w2_4k", n_layers=1)
     cache = make_cache(wl)
