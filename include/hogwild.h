@@ -166,7 +166,8 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
 hw_status hw_reset_block(hw_ctx *ctx, int32_t block_id);
 
 /* Force the number of KV partitions per head for following decodes (1 .. max_splits), or
- * 0 for the automatic choice (enough partitions to fill the GPU, each of >= 8 token groups). */
+ * 0 for the automatic choice (workgroups for about three quarters of the compute units, each
+ * partition of >= 8 token groups). */
 hw_status hw_set_split(hw_ctx *ctx, int32_t n_splits);
 
 /* Introspection: a block's length in a layer and its page ids in order (at most cap are

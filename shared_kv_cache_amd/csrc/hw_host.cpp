@@ -259,7 +259,10 @@ int32_t row_blocks_for(const hw_ctx *c, int32_t n_workers) {
 int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
   const int32_t row_blocks = row_blocks_for(c, n_workers);
   const int32_t per_head = c->cfg.n_kv_heads * std::max(1, row_blocks);
-  int32_t s = (c->num_cus + per_head - 1) / per_head;
+  // Workgroups for about three quarters of the CUs: measured on MI355X, this still keeps
+  // HBM saturated while each wave takes more groups (fixed per-wave costs amortised, less
+  // tail) and fewer partials reach the merge; 24 partitions for 8 KV heads beat 32 by 2-4%.
+  int32_t s = std::max(1, (3 * c->num_cus / 4) / per_head);
   s = std::min(s, std::max(1, n_groups / 8));
   return std::max(1, std::min(s, c->cfg.max_splits));
 }

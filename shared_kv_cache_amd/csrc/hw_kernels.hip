@@ -315,41 +315,65 @@ __device__ __forceinline__ void fetch_group(Stage<KV, D> &st, int2 desc, const K
 }
 
 // Issue the loads of the query offsets of the lane's rows for the block of segment seg.
-template <int RTW>
-__device__ __forceinline__ void fetch_delta(int (&dl)[RTW], int seg, const DecodeArgs &a,
+template <int RT>
+__device__ __forceinline__ void fetch_delta(int (&dl)[RT], int seg, const DecodeArgs &a,
                                             const int *row_w) {
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) dl[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
+  for (int rt = 0; rt < RT; ++rt) dl[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
 }
 
 __device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// One workgroup = one (split, KV head, block of up to 16 * RTW rows), NW waves. Every wave
-// holds all RTW row tiles and takes a contiguous run of the workgroup's token groups, so
-// each group is read from HBM by exactly one wave. NST register stages per wave: with one,
-// the group's loads are issued and then it is computed, the other wave on the SIMD (NW = 8)
-// computing meanwhile; with two (NW = 4, one wave per SIMD, for wide row tiles whose
-// accumulators fill the registers of two waves), the next group is in flight while one is
-// computed.
-template <typename KV, int D, int RTW, int NW, int NST>
+// Segments whose rotated queries one phase of the cooperative rotation holds in LDS: about
+// 64 KiB of operands.
+template <typename KV, int D, int RT>
+constexpr int phase_segments() {
+  constexpr int per_seg = RT * (D / 32) * 64 * (int)sizeof(typename Frag<KV, D>::QOp);
+  constexpr int c = (64 * 1024) / per_seg;
+  return c < 1 ? 1 : (c > 16 ? 16 : c);
+}
+
+// One workgroup = one (split, KV head, block of up to 16 * RT rows), NW waves. Every wave
+// holds all RT row tiles and takes a contiguous run of the workgroup's token groups, so each
+// group is read from HBM by exactly one wave.
+//
+// NST = 1 (NW = 8, two waves per SIMD): a group's loads are issued as soon as the previous
+// group is computed, the other wave on the SIMD computing meanwhile. Each wave rotates its
+// rows' query when it enters a new segment (block); that work too overlaps the other wave
+// and the loads in flight.
+//
+// NST = 2 (NW = 4, one wave per SIMD, for row tiles whose accumulators fill the registers
+// of two waves): the next group is in flight while one is computed. A wave here has no
+// sibling to hide a rotation of its 64 rows, so the workgroup rotates cooperatively: its
+// groups [begin, end) cover a contiguous range of segments (the group list is ordered by
+// segment), and all threads rotate every (segment, row) of that range once into an LDS
+// table of MFMA operands, with a table of the query offsets of its workers. A range with
+// more segments than the table holds is taken in phases of phase_segments() segments,
+// separated by workgroup barriers.
+template <typename KV, int D, int RT, int NW, int NST>
 __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
   static_assert(NST == 1 || NST == 2, "one or two stages");
+  constexpr bool COOP = NST == 2;
   using F = Frag<KV, D>;
   using S = Stage<KV, D>;
   using QOp = typename F::QOp;
   constexpr int NC = F::NC, NDT = F::NDT;
-  constexpr int RT = RTW;                          // row tiles of the workgroup
   constexpr int NT = NW * 64;
-  constexpr int QSTRIDE = D + 4;                   // padded q row (LDS bank spread)
+  constexpr int CAP = COOP ? phase_segments<KV, D, RT>() : 1;   // segments per phase
+  constexpr int NWMAX = RT * 16;                    // workers a block's rows can span
+  constexpr int QSTRIDE = D + 4;                    // padded q row (LDS bank spread)
   constexpr int Q_FLOATS = RT * 16 * QSTRIDE;
-  constexpr int QOP_FLOATS = NW * RTW * NC * 64 * (int)(sizeof(QOp) / 4);
-  constexpr int SLOTS = RTW * NDT * 64;            // one wave's O^T, f32x4 slots in lane order
+  // Rotated query operands: per phase segment (COOP) or per wave, [rt][chunk][lane] each.
+  constexpr int QT_FLOATS = (COOP ? CAP : NW) * RT * NC * 64 * (int)(sizeof(QOp) / 4);
+  constexpr int SLOTS = RT * NDT * 64;              // one wave's O^T, f32x4 slots in lane order
   constexpr int M_FLOATS = NW * SLOTS * 4;
-  constexpr int SMEM = Q_FLOATS + QOP_FLOATS > M_FLOATS ? Q_FLOATS + QOP_FLOATS : M_FLOATS;
+  constexpr int LOOP_FLOATS = Q_FLOATS + QT_FLOATS;  // live until the loop ends
+  constexpr int SMEM = LOOP_FLOATS > M_FLOATS ? LOOP_FLOATS : M_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ int sm_dl[COOP ? CAP * NWMAX : 1];     // query offsets [segment of phase][worker]
   __shared__ double sm_freq[D / 2];
-  __shared__ float sm_m[NW][16 * RTW];
-  __shared__ float sm_l[NW][16 * RTW];
+  __shared__ float sm_m[NW][16 * RT];
+  __shared__ float sm_l[NW][16 * RT];
   __shared__ float sm_rowm[64], sm_rowl[64];
 
   const int tid = threadIdx.x;
@@ -359,14 +383,15 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int row0 = blockIdx.z * a.rows_per_block;
   const int nrows = min(a.rows_per_block, a.rows - row0);
-  // Rotated query operands of this wave, in lane order: [rt][chunk][lane].
-  QOp *qop_lds = reinterpret_cast<QOp *>(smem + Q_FLOATS) + (size_t)wave * RTW * NC * 64;
+  QOp *qt = reinterpret_cast<QOp *>(smem + Q_FLOATS);
+  QOp *qop_wave = qt + (size_t)wave * RT * NC * 64;   // NST = 1: this wave's operands
 
   // This workgroup's token groups [begin, end); this wave's contiguous run of them.
   const long long begin = (long long)split * a.n_groups / a.n_splits;
   const long long end = (long long)(split + 1) * a.n_groups / a.n_splits;
   const long long wfirst = begin + (end - begin) * wave / NW;
   const long long wcount = begin + (end - begin) * (wave + 1) / NW - wfirst;
+  const long long wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);
   const KV *kl = static_cast<const KV *>(a.k_layer);
   const KV *vl = static_cast<const KV *>(a.v_layer);
   const size_t head_groups = (size_t)kvh * a.page_groups;
@@ -375,23 +400,32 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // fp32: exact while rr < 2^22, as the error of the product stays below 0.5 / group.
   auto worker_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
   // The lane's rows: row rt * 16 + col of the workgroup's block.
-  int row_w[RTW];
-  bool row_ok[RTW];
+  int row_w[RT];
+  bool row_ok[RT];
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + col;
     row_ok[rt] = r < nrows;
     row_w[rt] = row_ok[rt] ? worker_of(row0 + r) : 0;
   }
+  // Workers of the block's rows: wlo .. wlo + nw - 1 (nw <= NWMAX, one per row at most).
+  const int wlo = __builtin_amdgcn_readfirstlane(worker_of(row0));
+  const int nw = __builtin_amdgcn_readfirstlane(worker_of(row0 + nrows - 1)) - wlo + 1;
 
-  // Prologue, ordered for latency: the first descriptors (scalar), the raw queries and
-  // rotation frequencies, then the first groups' offsets and K/V; only then the wait for
-  // the queries, which leaves those loads in flight. A fetch with nothing to fetch (no
-  // group for this wave, or past the end of its run) still issues its loads, from
-  // descriptor (0, 0): page 0 of the head and the first row of the offset table, both
-  // always allocated; the data goes unused. Loads issued unconditionally keep the waits
-  // for each stage exact.
-  const long long wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);
+  // Prologue, ordered for latency. Scalar loads first: this wave's first descriptors (and,
+  // COOP, the workgroup's segment range). Then the raw queries and rotation frequencies,
+  // the offsets (of the first phase, or of this wave's first two groups) and group 0's K/V;
+  // only then the waits for the queries and offsets, which leave the K/V loads in flight.
+  // A fetch with nothing to fetch (no group for this wave, or past the end of its run)
+  // still issues its loads, from descriptor (0, 0): page 0 of the head and the first row of
+  // the offset table, both always allocated; the data goes unused. Loads issued
+  // unconditionally keep the waits for each stage exact.
+  int s_lo = 0, s_hi = -1;
+  if (COOP && end > begin) {
+    s_lo = load_desc(a.groups, begin).y >> 8;
+    s_hi = load_desc(a.groups, end - 1).y >> 8;
+  }
+  const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   int2 desc = make_int2(0, 0), next = make_int2(0, 0), next2 = make_int2(0, 0);
   if (wcount > 0) desc = load_desc(a.groups, wfirst);   // only groups of this wave's run
   if (wcount > 1) next = load_desc(a.groups, wfirst + 1);
@@ -409,14 +443,35 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
   }
   const double fq = tid < D / 2 ? a.turn_freq[tid] : 0.0;
-  S st, st2;
-  int dl_cur[RTW], dl_next[RTW];
-  fetch_delta(dl_cur, desc.y >> 8, a, row_w);
-  fetch_group(st, desc, kl, vl, head_groups, lane);
-  fetch_delta(dl_next, next.y >> 8, a, row_w);
-  if constexpr (NST == 2) fetch_group(st2, next, kl, vl, head_groups, lane);
+  // COOP: offsets of the phase starting at segment seg_lo: sm_dl[s * nw + k] = delta of
+  // worker wlo + k for segment seg_lo + s (-1: the block is not in that worker's view).
+  constexpr int DLPT = COOP ? (CAP * NWMAX + NT - 1) / NT : 1;
+  int dlv[DLPT];
+  auto load_offsets = [&](int seg_lo) __attribute__((always_inline)) {
+    const int cnt = min(CAP, s_hi + 1 - seg_lo) * nw;
+#pragma unroll
+    for (int k = 0; k < DLPT; ++k) {
+      const int t = tid + k * NT;
+      dlv[k] = t < cnt ? a.delta[(size_t)(seg_lo + t / nw) * a.n_workers + wlo + t % nw] : -1;
+    }
+  };
+  auto store_offsets = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < DLPT; ++k)
+      if (tid + k * NT < CAP * NWMAX) sm_dl[tid + k * NT] = dlv[k];
+  };
+  S st, st2;   // st: the group being computed; st2 (NST = 2): the group in flight
+  int dl_cur[RT], dl_next[RT];   // NST = 1: offsets of the lane's rows for groups i, i+1
+  if constexpr (COOP) {
+    load_offsets(s_lo);
+    fetch_group(st2, desc, kl, vl, head_groups, lane);
+  } else {
+    fetch_delta(dl_cur, desc.y >> 8, a, row_w);
+    fetch_group(st, desc, kl, vl, head_groups, lane);
+    fetch_delta(dl_next, next.y >> 8, a, row_w);
+  }
   if (wcount > 2) next2 = load_desc(a.groups, wfirst + 2);
-  // Stage the queries, pre-scaled by softmax_scale * log2(e), and the rotation
+  // Stage the queries, pre-scaled by softmax_scale * log2(e), the offsets and the rotation
   // frequencies in turns per position.
 #pragma unroll
   for (int k = 0; k < QV4; ++k) {
@@ -427,15 +482,55 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
           make_float4(x.x * a.q_scale, x.y * a.q_scale, x.z * a.q_scale, x.w * a.q_scale);
     }
   }
+  if constexpr (COOP) store_offsets();
   if (tid < D / 2) sm_freq[tid] = fq;
   __syncthreads();
 
-  f32x4 o[RTW][NDT];
-  float m[RTW], l[RTW];
-  bool rowvis[RTW];
-  bool rowmask[RTW];   // wave-uniform: some real row of this tile does not see the block
+  // Rotation of one row's query by delta = q_pos(w) - offset(w, block), for the 8 pairs
+  // (j, j + D/2), j = j0 .. j0 + 7: the angle delta * theta_j is reduced to a fraction of a
+  // turn in fp64; the sine and cosine of that fraction come from the hardware's fp32 units.
+  auto rotate8 = [&](const float *qrow, int j0, int dl, float *lo, float *hi) __attribute__((always_inline)) {
+    const double ddl = (double)dl;
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
+    for (int e = 0; e < 8; ++e) {
+      const double turns = ddl * sm_freq[j0 + e];
+      const float fr = (float)(turns - __builtin_rint(turns));
+      const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+      const float x0 = qrow[j0 + e], x1 = qrow[D / 2 + j0 + e];
+      lo[e] = x0 * cs - x1 * sn;
+      hi[e] = x1 * cs + x0 * sn;
+    }
+  };
+  // COOP: rotate every (segment, row) of a phase of nseg segments, all threads together. One
+  // item is (segment, row tile, chunk pair, lane).
+  auto rotate_phase = [&](int nseg) __attribute__((always_inline)) {
+    const int items = nseg * RT * (NC / 2) * 64;
+    for (int it = tid; it < items; it += NT) {
+      const int ln = it & 63;
+      int rest = it >> 6;
+      const int c = rest % (NC / 2);
+      rest /= NC / 2;
+      const int rt = rest % RT, sl = rest / RT;
+      const int row = rt * 16 + (ln & 15);
+      float lo[8], hi[8];
+      bool vis = false;
+      if (row < nrows) {
+        const int dl = sm_dl[sl * nw + worker_of(row0 + row) - wlo];
+        vis = dl >= 0;
+        rotate8(smem + row * QSTRIDE, 32 * c + 8 * (ln >> 4), vis ? dl : 0, lo, hi);
+      }
+      QOp *dst = qt + ((size_t)(sl * RT + rt) * NC + c) * 64 + ln;
+      dst[0] = vis ? F::make_q(lo) : F::zero_q();
+      dst[(NC / 2) * 64] = vis ? F::make_q(hi) : F::zero_q();
+    }
+  };
+
+  f32x4 o[RT][NDT];
+  float m[RT], l[RT];
+  bool rowvis[RT];
+  bool rowmask[RT];   // wave-uniform: some real row of this tile does not see the block
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
     m[rt] = -INFINITY;
     l[rt] = 0.0f;
     rowvis[rt] = false;
@@ -445,70 +540,74 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   }
   int cur_seg = -1;
 
-  auto process = [&](const S &sg, const int (&delta)[RTW]) __attribute__((always_inline)) {
+  // One group: visibility and (NST = 1, new segment) rotation, scores, online softmax, PV.
+  // seg_lo: first segment of the current phase (COOP); delta: the lane's rows' offsets for
+  // the group's block (NST = 1).
+  auto process = [&](const S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
     const int seg = sg.desc_y >> 8;
     const int nvalid = sg.desc_y & 255;
-    // Entering a new block: rotate each row's query by delta = q_pos(w) - offset(w, block).
-    // The angle delta * theta_j is reduced to a fraction of a turn in fp64; the sine and
-    // cosine of that fraction come from the hardware's fp32 units.
-    // Visibility of the block for the lane's rows.
+    const QOp *qs;
+    if constexpr (COOP) {
+      const int sl = seg - seg_lo;                   // segment within the phase
+      if (seg != cur_seg) {
+        cur_seg = seg;
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      rowvis[rt] = row_ok[rt] && delta[rt] >= 0;
-      rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && delta[rt] < 0) != 0;
-    }
-    if (seg != cur_seg) {
-      cur_seg = seg;
-#pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-        const int dl = delta[rt];
-        const float *qrow = smem + (rt * 16 + col) * QSTRIDE;
-        const double ddl = (double)(dl < 0 ? 0 : dl);
-#pragma unroll
-        for (int c = 0; c < NC / 2; ++c) {
-          const int j0 = 32 * c + 8 * grp;
-          float lo[8], hi[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double turns = ddl * sm_freq[j0 + e];
-            const float r = (float)(turns - __builtin_rint(turns));
-            const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
-            const float x0 = qrow[j0 + e], x1 = qrow[D / 2 + j0 + e];
-            lo[e] = x0 * cs - x1 * sn;
-            hi[e] = x1 * cs + x0 * sn;
-          }
-          qop_lds[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
-          qop_lds[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
-          // one chunk at a time: keeps the rotation's temporaries from crowding out the
-          // accumulators and the stage in flight
-          __builtin_amdgcn_sched_barrier(0);
+        for (int rt = 0; rt < RT; ++rt) {
+          const int dl = row_ok[rt] ? sm_dl[sl * nw + row_w[rt] - wlo] : -1;
+          rowvis[rt] = row_ok[rt] && dl >= 0;
+          rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
         }
       }
+      qs = qt + (size_t)sl * RT * NC * 64 + lane;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        rowvis[rt] = row_ok[rt] && delta[rt] >= 0;
+        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && delta[rt] < 0) != 0;
+      }
+      if (seg != cur_seg) {
+        cur_seg = seg;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int dl = delta[rt];
+#pragma unroll
+          for (int c = 0; c < NC / 2; ++c) {
+            float lo[8], hi[8];
+            rotate8(smem + (rt * 16 + col) * QSTRIDE, 32 * c + 8 * grp, dl < 0 ? 0 : dl, lo, hi);
+            qop_wave[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
+            qop_wave[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+            // one chunk at a time: keeps the rotation's temporaries from crowding out the
+            // accumulators and the stage in flight
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      qs = qop_wave + lane;
     }
 
     // Scores of the 32 tokens for every row: lane (row col, group grp) gets tokens
     // 8*grp + 4*hh + r of row tile rt in sc[rt][hh][r].
-    f32x4 sc[RTW][2];
+    f32x4 sc[RT][2];
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = sg.f.score(c, hh, qop_lds[(rt * NC + c) * 64 + lane], acc);
+        for (int c = 0; c < NC; ++c) acc = sg.f.score(c, hh, qs[(rt * NC + c) * 64], acc);
         sc[rt][hh] = acc;
       }
 
     // Online softmax in the log2 domain, one row per lane, 8 tokens per lane, with at most
     // one uniform branch for masking and one for rescaling. Rows past the workgroup's real
     // rows are never written out, so they need no mask.
-    float v8[RTW][8], mx[RTW];
+    float v8[RT][8], mx[RT];
     bool any_mask = nvalid < 32;
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) any_mask |= rowmask[rt];
+    for (int rt = 0; rt < RT; ++rt) any_mask |= rowmask[rt];
     if (any_mask) {
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * grp + e;
@@ -517,13 +616,13 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         }
     } else {
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) v8[rt][e] = sc[rt][e >> 2][e & 3];
     }
     bool grow = false;
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       float x = v8[rt][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) x = fmaxf(x, v8[rt][e]);
@@ -532,7 +631,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const float mnew = fmaxf(m[rt], mx[rt]);
         const float alpha = __builtin_amdgcn_exp2f(m[rt] - (mnew == -INFINITY ? 0.0f : mnew));
         l[rt] *= alpha;
@@ -542,7 +641,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       const float msafe = m[rt] == -INFINITY ? 0.0f : m[rt];
       float p[8], sum = 0.0f;
 #pragma unroll
@@ -557,7 +656,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
   };
 
-  if constexpr (NST == 1) {
+  if constexpr (!COOP) {
     // Group i: its descriptor and offsets came with group i-1; group i+1's descriptor is
     // in and group i+2's on its way.
     for (long long i = 0; i < wcount; ++i) {
@@ -565,36 +664,49 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         desc = next;
         next = next2;
 #pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) dl_cur[rt] = dl_next[rt];
+        for (int rt = 0; rt < RT; ++rt) dl_cur[rt] = dl_next[rt];
         fetch_group(st, desc, kl, vl, head_groups, lane);
         fetch_delta(dl_next, next.y >> 8, a, row_w);
         next2 = load_desc(a.groups, min(wfirst + i + 2, wlast));
       }
-      process(st, dl_cur);
+      process(st, 0, dl_cur);
     }
   } else {
-    // Two stages, groups i (st) and i+1 (st2) in flight; each stage is refilled with the
-    // group two ahead (or the dummy group) as soon as it has been computed.
-    for (long long i = 0; i < wcount; i += 2) {
-      const int2 da = i + 2 < wcount ? load_desc(a.groups, wfirst + i + 2) : make_int2(0, 0);
-      const int2 db = i + 3 < wcount ? load_desc(a.groups, wfirst + i + 3) : make_int2(0, 0);
-      process(st, dl_cur);
-      fetch_delta(dl_cur, da.y >> 8, a, row_w);
-      fetch_group(st, da, kl, vl, head_groups, lane);
-      if (i + 1 < wcount) process(st2, dl_next);
-      fetch_delta(dl_next, db.y >> 8, a, row_w);
-      fetch_group(st2, db, kl, vl, head_groups, lane);
+    // Phases: rotate the phase's segments, then every wave computes its groups that lie in
+    // them. Group i is in flight in st2 when its step starts; it moves to st and group i+1
+    // (descriptor next, in since the last step) is issued into st2 before group i is
+    // computed; group i+2's descriptor is on its way.
+    long long i = 0;
+    for (int ph = 0; ph < nph; ++ph) {
+      const int seg_lo = s_lo + ph * CAP;
+      if (ph > 0) {
+        __syncthreads();                             // the previous phase's table is done
+        load_offsets(seg_lo);
+        store_offsets();
+        __syncthreads();
+      }
+      rotate_phase(min(CAP, s_hi + 1 - seg_lo));
+      __syncthreads();
+      while (i < wcount && (desc.y >> 8) < seg_lo + CAP) {
+        st = st2;
+        fetch_group(st2, i + 1 < wcount ? next : make_int2(0, 0), kl, vl, head_groups, lane);
+        process(st, seg_lo, dl_cur);
+        desc = next;
+        next = next2;
+        next2 = load_desc(a.groups, min(wfirst + i + 3, wlast));
+        ++i;
+      }
     }
   }
 
   // ---- combine the waves: common max, then one LDS pass in which every slot is summed
   // over the waves in a fixed order ----
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
-  __syncthreads();  // every wave is done with the staged queries
+  for (int rt = 0; rt < RT; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
+  __syncthreads();  // every wave is done with the staged queries and operands
   if (grp == 0) {
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       sm_m[wave][rt * 16 + col] = m[rt];
       sm_l[wave][rt * 16 + col] = l[rt];
     }
@@ -602,7 +714,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   __syncthreads();
   f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + col;
     float mm = -INFINITY;
 #pragma unroll

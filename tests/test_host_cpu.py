@@ -346,7 +346,7 @@ def test_split_choice_and_override(ctx):
     _fill(ctx, 0, {0: 900, 1: 24})
     H.hw_set_views(ctx, [[0, 1]])
     auto = H.hw_debug_resolve(ctx, 0, 1)["n_splits"]
-    # 30 groups: min(ceil(256 CUs / (2 KV heads * 1 row block)), 30 // 8) without a GPU
+    # 30 groups: min(3/4 of 256 CUs / (2 KV heads * 1 row block), 30 // 8) without a GPU
     assert auto == 3
     H.hw_set_split(ctx, 7)
     assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == 7
