@@ -103,7 +103,8 @@ hw_status hw_create(const hw_config *cfg, hw_ctx **out);
 hw_status hw_destroy(hw_ctx *ctx);
 
 /* Text of the last error on ctx ("" if none); owned by ctx, valid until its next call.
- * With ctx == NULL: the last error of a failed hw_create on this thread. */
+ * With ctx == NULL: the last error of a failed context-free call (hw_create, or the
+ * streaming-read probe of hogwild_debug.h) on this thread. */
 const char *hw_last_error(const hw_ctx *ctx);
 
 /* Bytes of device workspace the context needs: the fp32 cos/sin table

@@ -1,8 +1,8 @@
 /*
  * hogwild_debug.h -- host-only introspection of the Hogwild! decode library, for tests.
  *
- * Apart from the two profiling hooks at the end, these calls touch no GPU and enqueue
- * nothing, so the host logic (slot assignment, page
+ * Apart from the profiling hooks and the streaming-read probe at the end, these calls touch
+ * no GPU and enqueue nothing, so the host logic (slot assignment, page
  * allocation, view resolution, validation) can be checked bit-exactly on a machine without
  * a GPU. Same status codes and validation rules as hogwild.h.
  */
@@ -50,6 +50,19 @@ hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity);
  * duration of that call's concurrent_decode kernel. *n receives the number of recorded
  * calls; recording then restarts at zero. */
 hw_status hw_debug_kernel_elapsed(hw_ctx *ctx, float *decode_ms, int32_t cap, int32_t *n);
+
+/* Measurement aid, independent of any context: n_blocks workgroups of 256 threads read the
+ * `bytes` bytes at `src` (device, 16-byte aligned, bytes a positive multiple of 16) once,
+ * each workgroup a contiguous 1/n_blocks of them, with 16-byte streaming loads, four in
+ * flight per thread. Nothing is written unless an impossible checksum turns up (then one
+ * float per workgroup goes to sink[n_blocks], device); the read bandwidth it achieves is the
+ * streaming ceiling the decode kernel is compared with. Enqueued on `stream`. elapsed_ms:
+ * NULL, or it receives the kernel's duration from start/stop events recorded by the
+ * kernel's own dispatch, and the call then waits for the kernel.
+ * Errors: HW_ERR_INVALID_ARG (pointers, alignment, sizes, n_blocks outside 1..65535),
+ * HW_ERR_HIP; hw_last_error(NULL) then explains, on the calling thread. */
+hw_status hw_debug_stream_read(const void *src, size_t bytes, float *sink, int32_t n_blocks,
+                               void *stream, float *elapsed_ms);
 
 #ifdef __cplusplus
 }

@@ -725,6 +725,34 @@ hw_status hw_debug_kernel_elapsed(hw_ctx *ctx, float *decode_ms, int32_t cap, in
   return HW_OK;
 }
 
+hw_status hw_debug_stream_read(const void *src, size_t bytes, float *sink, int32_t n_blocks,
+                               void *stream, float *elapsed_ms) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || (uintptr_t)src % 16 || n_blocks < 1 ||
+      n_blocks > 65535) {
+    g_create_error = "hw_debug_stream_read: bad pointer, alignment, size or n_blocks";
+    return HW_ERR_INVALID_ARG;
+  }
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  auto fail = [&](hipError_t e, const char *what) {
+    g_create_error = std::string("hw_debug_stream_read: ") + what + ": " + hipGetErrorString(e);
+    for (hipEvent_t x : ev)
+      if (x) (void)hipEventDestroy(x);
+    return HW_ERR_HIP;
+  };
+  hipError_t e;
+  if (elapsed_ms)
+    for (hipEvent_t &x : ev)
+      if ((e = hipEventCreate(&x)) != hipSuccess) return fail(e, "hipEventCreate");
+  e = hw::launch_stream_read(src, bytes, sink, n_blocks, (hipStream_t)stream, ev[0], ev[1]);
+  if (e != hipSuccess) return fail(e, "launch");
+  if (elapsed_ms) {
+    if ((e = hipEventSynchronize(ev[1])) != hipSuccess) return fail(e, "hipEventSynchronize");
+    if ((e = hipEventElapsedTime(elapsed_ms, ev[0], ev[1])) != hipSuccess) return fail(e, "hipEventElapsedTime");
+    for (hipEvent_t x : ev) (void)hipEventDestroy(x);
+  }
+  return HW_OK;
+}
+
 hw_status hw_reset_block(hw_ctx *ctx, int32_t block_id) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   if (block_id < 0 || block_id >= ctx->cfg.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "block id out of range");

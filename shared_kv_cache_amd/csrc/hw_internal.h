@@ -77,6 +77,8 @@ struct MergeArgs {
 };
 
 hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
+hipError_t launch_stream_read(const void *src, size_t bytes, float *sink, int n_blocks, hipStream_t s,
+                              hipEvent_t ev_start, hipEvent_t ev_stop);
 // ev_start/ev_stop: optional events recorded by the kernel's own dispatch (may be null).
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
                          hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);

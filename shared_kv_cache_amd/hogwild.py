@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_reset_block",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
-           "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed"]
+           "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
+           "hw_debug_stream_read"]
 
 
 class HwConfig(ctypes.Structure):
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_debug_resolve": (c_int, [c_void_p, c_int32, P32, P32, c_int32, P32, P32, c_int32, P32, P32]),
         "hw_debug_kernel_events": (c_int, [c_void_p, c_int32]),
         "hw_debug_kernel_elapsed": (c_int, [c_void_p, POINTER(c_float), c_int32, P32]),
+        "hw_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p,
+                                         POINTER(c_float)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -208,6 +211,19 @@ def hw_debug_kernel_elapsed(ctx, cap: int = 1 << 16):
     n = c_int32()
     _check(ctx, load_library().hw_debug_kernel_elapsed(ctx, dec, cap, ctypes.byref(n)))
     return list(dec[:min(n.value, cap)])
+
+
+def hw_debug_stream_read(src_ptr: int, nbytes: int, sink_ptr: int, n_blocks: int, stream,
+                         timed: bool = False):
+    """Enqueue the streaming-read probe; with timed, wait for it and return its duration in ms
+    (from events recorded by its own dispatch)."""
+    lib = load_library()
+    ms = c_float()
+    st = lib.hw_debug_stream_read(c_void_p(src_ptr), nbytes, c_void_p(sink_ptr), n_blocks,
+                                  c_void_p(stream), ctypes.byref(ms) if timed else None)
+    if st != HW_OK:
+        raise HwError(st, lib.hw_last_error(None).decode())
+    return ms.value if timed else None
 
 
 # ---------------------------------------------------------------- owner

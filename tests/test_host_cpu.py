@@ -354,3 +354,20 @@ def test_split_choice_and_override(ctx):
         H.hw_set_split(ctx, 257)
     H.hw_set_split(ctx, 0)
     assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == auto
+
+
+@pytest.mark.parametrize("src,nbytes,sink,n_blocks", [
+    (0, 1 << 20, 4096, 4),          # no source
+    (4096, 1 << 20, 0, 4),          # no sink
+    (4100, 1 << 20, 4096, 4),       # source not 16-byte aligned
+    (4096, 1000, 4096, 4),          # size not a multiple of 16
+    (4096, 0, 4096, 4),             # empty
+    (4096, 1 << 20, 4096, 0),       # no workgroups
+    (4096, 1 << 20, 4096, 65536),   # too many workgroups
+])
+def test_stream_read_probe_rejects_bad_arguments(src, nbytes, sink, n_blocks):
+    # validated on the host before any HIP call, so no GPU is needed and nothing is enqueued
+    with pytest.raises(H.HwError) as e:
+        H.hw_debug_stream_read(src, nbytes, sink, n_blocks, 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    assert "hw_debug_stream_read" in H.hw_last_error(None)
