@@ -39,6 +39,19 @@ hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *d
                            int32_t cap_segs, int32_t *n_segs, int32_t *groups,
                            int32_t cap_groups, int32_t *n_groups, int32_t *n_splits);
 
+/* The partition of a group list into KV partitions that hw_concurrent_decode uses (host
+ * only, no context). block_first[n_groups]: 1 where a group starts a new block of the union
+ * (group 0 always counts as one). A partition costs 1 per group plus alpha per block it
+ * touches; bounds[n_splits + 1] receives cuts 0 = bounds[0] <= ... <= bounds[n_splits] =
+ * n_groups (partition p = groups [bounds[p], bounds[p + 1]); trailing ones may be empty)
+ * whose largest partition cost is minimal up to one group's cost. Decodes use alpha 0 for
+ * up to 32 rows per workgroup and a measured per-block weight for the cooperative kernels
+ * (33..64 bf16 rows), with at most 255 partitions (beyond that, uniform cuts
+ * p * n_groups / n_splits). Errors: HW_ERR_INVALID_ARG (n_groups < 0, n_splits < 1,
+ * alpha < 0 or NaN, NULL arrays); hw_last_error(NULL) then explains. */
+hw_status hw_debug_partition(const uint8_t *block_first, int32_t n_groups, int32_t n_splits,
+                             double alpha, int32_t *bounds);
+
 /* ---- profiling hooks (these two do call HIP) ---------------------------------------------
  * With capacity > 0, each following hw_concurrent_decode has its concurrent_decode kernel
  * (not the split merge that follows it) record a start and a stop HIP event with its own

@@ -87,6 +87,11 @@ struct hw_ctx {
   bool uploaded_valid = false;
   int32_t up_n_groups = 0, up_n_seg = 0, up_n_workers = 0;
   size_t up_groups_off = 0;  // byte offset of the group list inside the tables region
+  std::vector<uint8_t> up_seg_first;   // per group: 1 if it starts a block of the union
+  // partition bounds of the uploaded group list, for bounds_splits partitions at bounds_alpha
+  std::vector<int32_t> bounds;
+  int32_t bounds_splits = -1;
+  double bounds_alpha = -1.0;
 
   // pinned staging ring
   char *staging = nullptr;
@@ -254,6 +259,61 @@ void commit_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *id
 int32_t row_blocks_for(const hw_ctx *c, int32_t n_workers) {
   const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
   return std::max(1, (rows_total(c, n_workers) + rpb - 1) / rpb);
+}
+
+// Cost of a partition: one per token group, plus alpha per block of the union it touches
+// (the rotation work of entering a block: once per workgroup in the cooperative kernels).
+// Cuts [0, G) into n contiguous partitions with the largest cost (nearly) minimal: bisection
+// on the cost bound, greedy packing at each bound (greedy is within one group's cost of the
+// optimum). Trailing partitions may be empty.
+bool pack_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, double cap,
+                 int32_t *out) {
+  int32_t p = 0;
+  out[0] = 0;
+  double cost = 0.0;
+  for (int32_t i = 0; i < G; ++i) {
+    const bool open = i == out[p];
+    const double add = 1.0 + ((open || first[i]) ? alpha : 0.0);
+    if (!open && cost + add > cap) {
+      if (++p >= n) return false;
+      out[p] = i;
+      cost = 1.0 + alpha;
+    } else {
+      cost += add;
+    }
+  }
+  for (int32_t q = p + 1; q <= n; ++q) out[q] = G;
+  return true;
+}
+
+void partition_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, int32_t *out) {
+  if (G <= 0) {
+    for (int32_t q = 0; q <= n; ++q) out[q] = 0;
+    return;
+  }
+  int64_t starts = 0;
+  for (int32_t i = 0; i < G; ++i) starts += (first[i] || i == 0) ? 1 : 0;
+  double lo = std::max(1.0 + alpha, ((double)G + alpha * (double)starts) / (double)n);
+  double hi = lo + 2.0 * (1.0 + alpha);
+  while (!pack_bounds(first, G, n, alpha, hi, out)) hi *= 2.0;
+  for (int it = 0; it < 40 && hi - lo > 1e-6; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (pack_bounds(first, G, n, alpha, mid, out)) hi = mid;
+    else lo = mid;
+  }
+  pack_bounds(first, G, n, alpha, hi, out);
+}
+
+// Weight of a block entry in group units, by kernel shape. Cooperative kernels (33..64 bf16
+// rows) rotate every block of a partition before streaming it; measured on MI355X, a
+// partition's extra block costs it about the time of this many groups.
+#ifndef HW_SPLIT_ALPHA_COOP
+#define HW_SPLIT_ALPHA_COOP 2.0
+#endif
+double split_alpha(const hw_ctx *c, int32_t rows) {
+  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
+  const int32_t first = std::min(rows, rpb);
+  return (c->cfg.kv_dtype == HW_BF16 && first > 32) ? HW_SPLIT_ALPHA_COOP : 0.0;
 }
 
 int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
@@ -616,10 +676,13 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     if (n_seg) std::memcpy(stg, r.delta.data(), (size_t)n_seg * n * sizeof(int32_t));
     int32_t *gd = reinterpret_cast<int32_t *>(stg + delta_bytes);
     const int32_t gpp = g.page_size / hw::kTokGroup;
+    ctx->up_seg_first.assign((size_t)n_groups, 0);
     for (int32_t i = 0; i < n_groups; ++i) {
       gd[2 * i] = r.g_page[i] * g.n_kv_heads * gpp + r.g_gip[i];
       gd[2 * i + 1] = (r.g_seg[i] << 8) | r.g_valid[i];
+      ctx->up_seg_first[i] = (i == 0 || r.g_seg[i] != r.g_seg[i - 1]) ? 1 : 0;
     }
+    ctx->bounds_splits = -1;
     if (bytes) {
       hipError_t e = hipMemcpyAsync(tables, stg, bytes, hipMemcpyHostToDevice, s);
       if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpyAsync(view tables)");
@@ -662,6 +725,16 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.rows_per_block = hw::rows_per_block(g.kv_dtype);
   a.inv_group = 1.0f / (float)group;
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
+  if (splits <= hw::kMaxBoundSplits) {
+    const double alpha = split_alpha(ctx, rows);
+    if (ctx->bounds_splits != splits || ctx->bounds_alpha != alpha) {
+      ctx->bounds.resize((size_t)splits + 1);
+      partition_bounds(ctx->up_seg_first.data(), n_groups, splits, alpha, ctx->bounds.data());
+      ctx->bounds_splits = splits;
+      ctx->bounds_alpha = alpha;
+    }
+    std::copy(ctx->bounds.begin(), ctx->bounds.end(), a.split_begin);
+  }
   const int32_t row_blocks = row_blocks_for(ctx, n);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
   hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
@@ -812,6 +885,16 @@ hw_status hw_debug_reserve(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const i
     runs[5 * i + 4] = r.pos0;
   }
   commit_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
+  return HW_OK;
+}
+
+hw_status hw_debug_partition(const uint8_t *block_first, int32_t n_groups, int32_t n_splits,
+                             double alpha, int32_t *bounds) {
+  if (n_groups < 0 || n_splits < 1 || !(alpha >= 0.0) || !bounds || (n_groups > 0 && !block_first)) {
+    g_create_error = "hw_debug_partition: invalid argument";
+    return HW_ERR_INVALID_ARG;
+  }
+  partition_bounds(block_first, n_groups, n_splits, alpha, bounds);
   return HW_OK;
 }
 

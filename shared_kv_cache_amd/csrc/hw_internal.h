@@ -15,6 +15,7 @@ constexpr int kRowsPerBlockF32 = 16;   // the same for fp32 pools (exact-check p
 
 inline int rows_per_block(hw_dtype dt) { return dt == HW_F32 ? kRowsPerBlockF32 : kRowsPerBlock; }
 constexpr int kMaxRunsPerLaunch = 64;  // append runs carried in one launch's arguments
+constexpr int kMaxBoundSplits = 255;   // partitions whose group bounds ride in the launch arguments
 
 // One run of appended tokens: consecutive tokens of one block inside one page.
 struct AppendRun {
@@ -59,6 +60,9 @@ struct DecodeArgs {
   int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)
   float inv_group;         // 1 / group (rows < 2^22, so the worker of a row is exact in fp32)
   float q_scale;           // softmax_scale * log2(e)
+  // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
+  // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
+  int32_t split_begin[kMaxBoundSplits + 1];
 };
 
 

@@ -387,8 +387,9 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   QOp *qop_wave = qt + (size_t)wave * RT * NC * 64;   // NST = 1: this wave's operands
 
   // This workgroup's token groups [begin, end); this wave's contiguous run of them.
-  const long long begin = (long long)split * a.n_groups / a.n_splits;
-  const long long end = (long long)(split + 1) * a.n_groups / a.n_splits;
+  const bool bounded = a.n_splits <= kMaxBoundSplits;
+  const long long begin = bounded ? a.split_begin[split] : (long long)split * a.n_groups / a.n_splits;
+  const long long end = bounded ? a.split_begin[split + 1] : (long long)(split + 1) * a.n_groups / a.n_splits;
   const long long wfirst = begin + (end - begin) * wave / NW;
   const long long wcount = begin + (end - begin) * (wave + 1) / NW - wfirst;
   const long long wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);

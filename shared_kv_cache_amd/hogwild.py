@@ -28,7 +28,7 @@ EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_reset_block",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
            "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
-           "hw_debug_stream_read"]
+           "hw_debug_stream_read", "hw_debug_partition"]
 
 
 class HwConfig(ctypes.Structure):
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_debug_kernel_elapsed": (c_int, [c_void_p, POINTER(c_float), c_int32, P32]),
         "hw_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p,
                                          POINTER(c_float)]),
+        "hw_debug_partition": (c_int, [POINTER(ctypes.c_uint8), c_int32, c_int32, ctypes.c_double,
+                                       P32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -200,6 +202,19 @@ def hw_debug_resolve(ctx, layer: int, n_workers: int, cap_segs: int = 4096,
             "delta": [list(delta[s * n_workers:(s + 1) * n_workers]) for s in range(ns)],
             "n_segs": n_seg.value, "n_groups": n_grp.value, "n_splits": n_split.value,
             "groups": [tuple(groups[4 * i:4 * i + 4]) for i in range(n_grp.value)]}
+
+
+def hw_debug_partition(block_first, n_splits: int, alpha: float):
+    """Partition bounds (list of n_splits + 1 cuts) of a group list whose block starts are
+    flagged in block_first (sequence of 0/1)."""
+    lib = load_library()
+    g = len(block_first)
+    first = (ctypes.c_uint8 * max(1, g))(*[1 if x else 0 for x in block_first])
+    out = (c_int32 * (n_splits + 1))()
+    st = lib.hw_debug_partition(first if g else None, g, n_splits, ctypes.c_double(alpha), out)
+    if st != HW_OK:
+        raise HwError(st, lib.hw_last_error(None).decode())
+    return list(out)
 
 
 def hw_debug_kernel_events(ctx, capacity: int) -> None:

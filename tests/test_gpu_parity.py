@@ -201,22 +201,35 @@ def _variant_workload(head_dim, n_workers, group):
                          "n_workers": n_workers, "n_q_heads": 2 * group, "n_kv_heads": 2,
                          "head_dim": head_dim, "kv_dtype": "bf16", "value_scale": 1.0,
                          "inprogress": inprog, "lengths": lengths, "owners": owners,
-                         "n_pages": pages, "max_position": 2048})
+                         "n_pages": pages,
+                         "max_position": max(2048, -(-(sum(lengths.values()) + 1) // 1024) * 1024)})
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("n_workers,group", [(2, 8), (4, 8), (5, 8), (8, 8), (3, 5)])
+@pytest.mark.parametrize("n_workers,group", [(2, 8), (4, 8), (5, 8), (8, 8), (3, 5), (6, 8),
+                                             (7, 6), (16, 2), (9, 7), (32, 2), (64, 1), (13, 5)])
 def test_every_bf16_kernel_variant(head_dim, n_workers, group):
-    # 16, 32, 40, 64 and 15 rows per KV head: one to four 16-row tiles, i.e. the 8-wave
-    # single-stage kernels and the 4-wave two-stage kernels, each under automatic and
-    # forced KV partitions.
+    # 15 to 65 rows per KV head: one to four 16-row tiles, i.e. the 8-wave single-stage
+    # kernels and the 4-wave two-stage kernels, each under automatic and forced KV
+    # partitions (several rotation phases at one partition). Up to 8 workers per block of
+    # rows share one cos/sin table per (worker, block); 9 to 64 workers (groups of 1, 2, 5, 7)
+    # take the per-row rotation, and 13 workers of 5 heads mix both in one launch.
+    # Partition counts: automatic, 1, 3, 40 and 80 (bounds chosen by the host; many
+    # partitions empty at 80).
     wl = _variant_workload(head_dim, n_workers, group)
-    cache = make_cache(wl, max_blocks=n_workers + 2)
+    cache = make_cache(wl, max_blocks=n_workers + 2, max_splits=128)
     fill_layer(cache, wl, 0)
     cache.set_views(wl.views())
-    for splits in (0, 1, 3):
+    q = wl.q(0)
+    ref, ref_lse = O.concurrent_attention(q.astype(np.float64), oracle_blocks(wl, 0), wl.views(),
+                                          theta=wl.theta)
+    for splits in (0, 1, 3, 40, 80):
         H.hw_set_split(cache.ctx, splits)
-        _check_layer(cache, wl, 0)
+        out, lse = decode_np(cache, 0, q)
+        err = rel_l2(out, ref)
+        _say(f"{wl.name} splits {splits}: rel_l2 {err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
     cache.close()
 
 

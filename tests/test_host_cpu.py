@@ -371,3 +371,67 @@ def test_stream_read_probe_rejects_bad_arguments(src, nbytes, sink, n_blocks):
         H.hw_debug_stream_read(src, nbytes, sink, n_blocks, 0)
     assert e.value.status == H.HW_ERR_INVALID_ARG
     assert "hw_debug_stream_read" in H.hw_last_error(None)
+
+
+# ---- KV partitioning (host only) ----------------------------------------------------------
+
+def _partition_cost(first, a, b, alpha):
+    """Cost of partition [a, b): one per group plus alpha per block it touches."""
+    if b <= a:
+        return 0.0
+    return (b - a) + alpha * sum(1 for i in range(a, b) if i == a or first[i])
+
+
+def _best_max_cost(first, n, alpha):
+    """Brute force: the smallest largest-partition cost over all cut vectors."""
+    import itertools
+    g = len(first)
+    best = float("inf")
+    for cuts in itertools.combinations_with_replacement(range(g + 1), n - 1):
+        b = [0, *cuts, g]
+        best = min(best, max(_partition_cost(first, b[i], b[i + 1], alpha) for i in range(n)))
+    return best
+
+
+def test_partition_bounds_are_min_max_optimal():
+    rng = np.random.default_rng(7)
+    for case in range(60):
+        g = int(rng.integers(0, 13))
+        n = int(rng.integers(1, 5))
+        first = [1 if (i == 0 or rng.random() < 0.3) else 0 for i in range(g)]
+        alpha = float(rng.choice([0.0, 0.5, 2.0, 3.0]))
+        b = H.hw_debug_partition(first, n, alpha)
+        assert len(b) == n + 1 and b[0] == 0 and b[-1] == g
+        assert all(b[i] <= b[i + 1] for i in range(n)), b
+        got = max(_partition_cost(first, b[i], b[i + 1], alpha) for i in range(n)) if g else 0.0
+        want = _best_max_cost(first, n, alpha) if g else 0.0
+        assert got <= want + 1e-4, (case, first, n, alpha, b, got, want)
+
+
+def test_partition_without_block_weight_is_balanced():
+    # alpha 0: partitions of ceil(G / n) groups (the last one takes the remainder)
+    for g, n in [(1149, 24), (541, 24), (7, 3), (5, 8), (256, 256)]:
+        b = H.hw_debug_partition([1] + [0] * (g - 1), n, 0.0)
+        sizes = [b[i + 1] - b[i] for i in range(n)]
+        assert max(sizes) == -(-g // n) and sum(sizes) == g
+
+
+def test_partition_gives_block_rich_ranges_fewer_groups():
+    # a long block, then eight short ones (the shape of a common history followed by the
+    # workers' in-progress blocks): weighting blocks shrinks the partitions that hold them
+    lens = [1024, 11, 22, 18, 15, 22, 16, 3, 18]
+    first = []
+    for n_g in lens:
+        first += [1] + [0] * (n_g - 1)
+    b = H.hw_debug_partition(first, 24, 3.0)
+    sizes = [b[i + 1] - b[i] for i in range(24)]
+    assert max(sizes[-3:]) < min(sizes[:20])
+    worst = max(_partition_cost(first, b[i], b[i + 1], 3.0) for i in range(24))
+    assert worst <= 52.0 + 1e-6
+
+
+def test_partition_rejects_bad_arguments():
+    for args in [([1, 0], 0, 1.0), ([1, 0], 2, -1.0), ([1, 0], 2, float("nan"))]:
+        with pytest.raises(H.HwError) as e:
+            H.hw_debug_partition(*args)
+        assert e.value.status == H.HW_ERR_INVALID_ARG
