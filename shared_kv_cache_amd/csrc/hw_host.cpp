@@ -87,6 +87,7 @@ struct hw_ctx {
   bool uploaded_valid = false;
   int32_t up_n_groups = 0, up_n_seg = 0, up_n_workers = 0;
   size_t up_groups_off = 0;  // byte offset of the group list inside the tables region
+  int32_t up_stride = 2;     // ints per uploaded group descriptor
   std::vector<uint8_t> up_seg_first;   // per group: 1 if it starts a block of the union
   // partition bounds of the uploaded group list, for bounds_splits partitions at bounds_alpha
   std::vector<int32_t> bounds;
@@ -137,7 +138,7 @@ void layout_workspace(hw_ctx *c) {
   off = align_up(off + half * sizeof(double));
   c->off_tables = off;
   c->tables_bytes = align_up((size_t)g.max_blocks * g.max_workers * sizeof(int32_t)) +
-                    align_up(max_groups * 2 * sizeof(int32_t));
+                    align_up(max_groups * hw::kWideStride * sizeof(int32_t));
   off = align_up(off + c->tables_bytes);
   c->off_part_o = off;
   c->part_o_bytes = (size_t)g.max_splits * g.n_kv_heads * max_rows * g.head_dim * sizeof(float);
@@ -664,8 +665,14 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     if (st != HW_OK) return st;
     const int32_t n_seg = (int32_t)r.seg_blocks.size();
     const int32_t n_groups = (int32_t)r.g_page.size();
+    // Wide descriptors (each group's offsets beside it) for the 8-wave kernels when every
+    // worker fits; the cooperative kernels read the offset table per phase instead.
+    const int32_t rows_all = n * (g.n_q_heads / g.n_kv_heads);
+    const bool wide = n <= hw::kWideWorkers && hw::decode_waves(g.kv_dtype, rows_all) == 8 &&
+                      rows_all <= hw::rows_per_block(g.kv_dtype);
+    const int32_t stride = wide ? hw::kWideStride : 2;
     const size_t delta_bytes = align_up((size_t)n_seg * n * sizeof(int32_t));
-    const size_t bytes = delta_bytes + (size_t)n_groups * 2 * sizeof(int32_t);
+    const size_t bytes = delta_bytes + (size_t)n_groups * stride * sizeof(int32_t);
     const int slot = ctx->next_slot;
     ctx->next_slot = (ctx->next_slot + 1) % kStagingSlots;
     if (ctx->event_live[slot]) {
@@ -678,8 +685,12 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     const int32_t gpp = g.page_size / hw::kTokGroup;
     ctx->up_seg_first.assign((size_t)n_groups, 0);
     for (int32_t i = 0; i < n_groups; ++i) {
-      gd[2 * i] = r.g_page[i] * g.n_kv_heads * gpp + r.g_gip[i];
-      gd[2 * i + 1] = (r.g_seg[i] << 8) | r.g_valid[i];
+      int32_t *d = gd + (size_t)stride * i;
+      d[0] = r.g_page[i] * g.n_kv_heads * gpp + r.g_gip[i];
+      d[1] = (r.g_seg[i] << 8) | r.g_valid[i];
+      if (wide)
+        for (int32_t k = 0; k < hw::kWideWorkers; ++k)
+          d[2 + k] = k < n ? r.delta[(size_t)r.g_seg[i] * n + k] : -1;
       ctx->up_seg_first[i] = (i == 0 || r.g_seg[i] != r.g_seg[i - 1]) ? 1 : 0;
     }
     ctx->bounds_splits = -1;
@@ -696,6 +707,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     ctx->up_n_seg = n_seg;
     ctx->up_n_workers = n;
     ctx->up_groups_off = delta_bytes;
+    ctx->up_stride = stride;
   }
 
   const int32_t group = g.n_q_heads / g.n_kv_heads;
@@ -725,6 +737,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.rows_per_block = hw::rows_per_block(g.kv_dtype);
   a.inv_group = 1.0f / (float)group;
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
+  a.desc_stride = ctx->up_stride;
   if (splits <= hw::kMaxBoundSplits) {
     const double alpha = split_alpha(ctx, rows);
     if (ctx->bounds_splits != splits || ctx->bounds_alpha != alpha) {

@@ -14,8 +14,21 @@ constexpr int kRowsPerBlock = 64;      // stacked (worker, query head) rows per 
 constexpr int kRowsPerBlockF32 = 16;   // the same for fp32 pools (exact-check path; wider operands)
 
 inline int rows_per_block(hw_dtype dt) { return dt == HW_F32 ? kRowsPerBlockF32 : kRowsPerBlock; }
+// Waves per decode workgroup when each KV head has `rows` stacked rows (launch_decode's
+// choice): bf16 blocks of up to 32 rows run on 8 waves, of 33..64 rows on 4; fp32 on 8.
+inline int decode_waves(hw_dtype dt, int rows) {
+  const int first = rows < rows_per_block(dt) ? rows : rows_per_block(dt);
+  return (dt == HW_BF16 && first > 32) ? 4 : 8;
+}
 constexpr int kMaxRunsPerLaunch = 64;  // append runs carried in one launch's arguments
 constexpr int kMaxBoundSplits = 255;   // partitions whose group bounds ride in the launch arguments
+// Up to this many workers, 8-wave decodes read "wide" group descriptors: 8 ints per group,
+// {group index of head 0, segment << 8 | valid tokens, query offset of workers 0..5 for the
+// group's segment (-1: not visible; unused slots -1)}, so a group's offsets arrive with its
+// descriptor through the scalar cache.
+constexpr int kWideWorkers = 6;
+constexpr int kWideStride = 8;
+
 
 // One run of appended tokens: consecutive tokens of one block inside one page.
 struct AppendRun {
@@ -44,7 +57,8 @@ struct DecodeArgs {
   const float *q;          // [n_workers][n_q_heads][head_dim]
   float *out;              // [n_workers][n_q_heads][head_dim]   (written when n_splits == 1)
   float *lse;              // [n_workers][n_q_heads] or null      (idem)
-  const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens}
+  const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens},
+                           // or wide descriptors (desc_stride = kWideStride ints per group)
   const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
   const double *turn_freq; // [head_dim/2] theta^(-2j/d) / (2 pi): rotation turns per position
   float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
@@ -63,6 +77,7 @@ struct DecodeArgs {
   // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];
+  int32_t desc_stride;     // ints per group descriptor: 2, or kWideStride (8-wave kernels only)
 };
 
 

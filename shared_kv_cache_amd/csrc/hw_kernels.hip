@@ -187,6 +187,27 @@ struct Frag<__bf16, D> {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) v[dt] = ld16<NT>(vg + (dt * 64 + lane) * 8);
   }
+  // The same 16 loads straight into LDS (one 1 KiB slot per load, lane l's 16 bytes at
+  // l * 16), streaming hint; stage_read then picks up exactly what load would have given.
+  __device__ __forceinline__ static void load_lds(const __bf16 *kg, const __bf16 *vg, int lane,
+                                                  uint4 (*slot)[64]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        __builtin_amdgcn_global_load_lds(kg + ((c * 2 + hh) * 64 + lane) * 8, &slot[c * 2 + hh][0], 16, 0, 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      __builtin_amdgcn_global_load_lds(vg + (dt * 64 + lane) * 8, &slot[NC * 2 + dt][0], 16, 0, 2);
+  }
+  __device__ __forceinline__ void stage_read(const uint4 (*slot)[64], int lane) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) k[c][hh] = slot[c * 2 + hh][lane];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) v[dt] = slot[NC * 2 + dt][lane];
+  }
   static __device__ __forceinline__ QOp make_q(const float *x) {
     QOp r;
 #pragma unroll
@@ -297,6 +318,36 @@ __device__ __forceinline__ int2 load_desc(const int2 *groups, long long i) {
   return make_int2(p[2 * i], p[2 * i + 1]);
 }
 
+// A wide descriptor (kWideStride ints): the group's {x, y} and the query offsets of workers
+// 0..kWideWorkers-1 for its segment, all wave-uniform, in one scalar-cache read. The offsets
+// are kept as named fields (not an array) so that picking one per lane stays a register
+// select.
+static_assert(kWideWorkers == 6, "WideOff holds six offsets");
+struct WideOff {
+  int o0 = -1, o1 = -1, o2 = -1, o3 = -1, o4 = -1, o5 = -1;
+};
+__device__ __forceinline__ int2 load_desc_wide(const int2 *groups, long long i, WideOff &w) {
+  const ConstInt *p = (const ConstInt *)groups + (long long)kWideStride * i;
+  w.o0 = p[2];
+  w.o1 = p[3];
+  w.o2 = p[4];
+  w.o3 = p[5];
+  w.o4 = p[6];
+  w.o5 = p[7];
+  return make_int2(p[0], p[1]);
+}
+// (readfirstlane of the wave-uniform fields keeps the compiler from turning the selects
+// into one load at a computed offset, which would put the offsets in memory)
+__device__ __forceinline__ int wide_pick(const WideOff &w, int k) {
+  int v = __builtin_amdgcn_readfirstlane(w.o0);
+  v = k == 1 ? __builtin_amdgcn_readfirstlane(w.o1) : v;
+  v = k == 2 ? __builtin_amdgcn_readfirstlane(w.o2) : v;
+  v = k == 3 ? __builtin_amdgcn_readfirstlane(w.o3) : v;
+  v = k == 4 ? __builtin_amdgcn_readfirstlane(w.o4) : v;
+  v = k == 5 ? __builtin_amdgcn_readfirstlane(w.o5) : v;
+  return v;
+}
+
 // Per-wave pipeline state: one 32-token group's operands and its descriptor (wave-uniform).
 template <typename KV, int D>
 struct Stage {
@@ -350,9 +401,17 @@ constexpr int phase_segments() {
 // table of MFMA operands, with a table of the query offsets of its workers. A range with
 // more segments than the table holds is taken in phases of phase_segments() segments,
 // separated by workgroup barriers.
-template <typename KV, int D, int RT, int NW, int NST>
+//
+// WIDE (NST = 1, at most kWideWorkers workers, all rows in one block): the group list holds
+// wide descriptors, so each group's query offsets come with its descriptor through the
+// scalar cache instead of as vector loads queued behind the K/V traffic. With bf16 pools a
+// WIDE wave then also keeps its next group in flight while it computes one: the next group
+// streams straight into a per-wave LDS stage (LDS-DMA loads) and moves to registers once the
+// group is done; the rotated query operands stay in registers.
+template <typename KV, int D, int RT, int NW, int NST, bool WIDE>
 __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
   static_assert(NST == 1 || NST == 2, "one or two stages");
+  static_assert(!WIDE || NST == 1, "wide descriptors: single-stage kernels");
   constexpr bool COOP = NST == 2;
   using F = Frag<KV, D>;
   using S = Stage<KV, D>;
@@ -364,12 +423,20 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   constexpr int QSTRIDE = D + 4;                    // padded q row (LDS bank spread)
   constexpr int Q_FLOATS = RT * 16 * QSTRIDE;
   // Rotated query operands: per phase segment (COOP) or per wave, [rt][chunk][lane] each.
-  constexpr int QT_FLOATS = (COOP ? CAP : NW) * RT * NC * 64 * (int)(sizeof(QOp) / 4);
+  constexpr bool LDSST = WIDE && std::is_same<KV, __bf16>::value;   // LDS stage, see above
+  constexpr int NLOAD = NC * 2 + NDT;               // 16-byte loads per lane per group
+  constexpr int QT_FLOATS = LDSST ? 0 : (COOP ? CAP : NW) * RT * NC * 64 * (int)(sizeof(QOp) / 4);
+  constexpr int STAGE_FLOATS = LDSST ? NW * NLOAD * 64 * 4 : 0;
   constexpr int SLOTS = RT * NDT * 64;              // one wave's O^T, f32x4 slots in lane order
   constexpr int M_FLOATS = NW * SLOTS * 4;
-  constexpr int LOOP_FLOATS = Q_FLOATS + QT_FLOATS;  // live until the loop ends
+  // LDSST keeps the staged queries in an LDS array of their own, apart from the stage: the
+  // compiler orders reads of an array after the LDS fills into it, and the rotation must not
+  // wait for the group in flight.
+  constexpr int LOOP_FLOATS = (LDSST ? 0 : Q_FLOATS) + QT_FLOATS + STAGE_FLOATS;  // live until the loop ends
   constexpr int SMEM = LOOP_FLOATS > M_FLOATS ? LOOP_FLOATS : M_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ __attribute__((aligned(16))) float sm_q[LDSST ? Q_FLOATS : 4];
+  float *const qrows = LDSST ? sm_q : smem;   // staged queries [16 * RT][QSTRIDE]
   __shared__ int sm_dl[COOP ? CAP * NWMAX : 1];     // query offsets [segment of phase][worker]
   __shared__ double sm_freq[D / 2];
   __shared__ float sm_m[NW][16 * RT];
@@ -383,8 +450,11 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int row0 = blockIdx.z * a.rows_per_block;
   const int nrows = min(a.rows_per_block, a.rows - row0);
-  QOp *qt = reinterpret_cast<QOp *>(smem + Q_FLOATS);
-  QOp *qop_wave = qt + (size_t)wave * RT * NC * 64;   // NST = 1: this wave's operands
+  QOp *qt = reinterpret_cast<QOp *>(smem + (LDSST ? 0 : Q_FLOATS));
+  QOp *qop_wave = qt + (size_t)wave * RT * NC * 64;   // NST = 1 without LDSST: this wave's operands
+  // LDSST: this wave's stage, NLOAD slots of 64 lanes x 16 bytes
+  uint4 (*stage)[64] = reinterpret_cast<uint4 (*)[64]>(smem + QT_FLOATS) + wave * NLOAD;
+  QOp qreg[RT][NC];   // LDSST: the rotated query operands of the current segment
 
   // This workgroup's token groups [begin, end); this wave's contiguous run of them.
   const bool bounded = a.n_splits <= kMaxBoundSplits;
@@ -428,8 +498,19 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   int2 desc = make_int2(0, 0), next = make_int2(0, 0), next2 = make_int2(0, 0);
-  if (wcount > 0) desc = load_desc(a.groups, wfirst);   // only groups of this wave's run
-  if (wcount > 1) next = load_desc(a.groups, wfirst + 1);
+  // WIDE: the offsets of workers 0.. for the segments of desc, next, next2
+  WideOff ow, ow_next, ow_next2;
+  auto desc_at = [&](long long i, WideOff &off) __attribute__((always_inline)) {
+    if constexpr (WIDE) return load_desc_wide(a.groups, i, off);
+    else return load_desc(a.groups, i);
+  };
+  if (wcount > 0) desc = desc_at(wfirst, ow);   // only groups of this wave's run
+  if (wcount > 1) next = desc_at(wfirst + 1, ow_next);
+  // WIDE: the lane's rows' offsets (all rows in one block: worker index = row_w)
+  auto wide_rows = [&](int (&dl)[RT], const WideOff &off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) dl[rt] = wide_pick(off, row_w[rt]);
+  };
   constexpr int QV4 = (RT * 16 * D / 4 + NT - 1) / NT;   // float4 of queries per thread
   float4 qv[QV4];
 #pragma unroll
@@ -466,12 +547,15 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   if constexpr (COOP) {
     load_offsets(s_lo);
     fetch_group(st2, desc, kl, vl, head_groups, lane);
+  } else if constexpr (WIDE) {
+    fetch_group(st, desc, kl, vl, head_groups, lane);
+    wide_rows(dl_cur, ow);
   } else {
     fetch_delta(dl_cur, desc.y >> 8, a, row_w);
     fetch_group(st, desc, kl, vl, head_groups, lane);
     fetch_delta(dl_next, next.y >> 8, a, row_w);
   }
-  if (wcount > 2) next2 = load_desc(a.groups, wfirst + 2);
+  if (wcount > 2) next2 = desc_at(wfirst + 2, ow_next2);
   // Stage the queries, pre-scaled by softmax_scale * log2(e), the offsets and the rotation
   // frequencies in turns per position.
 #pragma unroll
@@ -479,7 +563,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     const int i = tid + k * NT;
     if (i < RT * 16 * D / 4) {
       const float4 x = qv[k];
-      *reinterpret_cast<float4 *>(smem + (i / (D / 4)) * QSTRIDE + (i % (D / 4)) * 4) =
+      *reinterpret_cast<float4 *>(qrows + (i / (D / 4)) * QSTRIDE + (i % (D / 4)) * 4) =
           make_float4(x.x * a.q_scale, x.y * a.q_scale, x.z * a.q_scale, x.w * a.q_scale);
     }
   }
@@ -518,7 +602,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       if (row < nrows) {
         const int dl = sm_dl[sl * nw + worker_of(row0 + row) - wlo];
         vis = dl >= 0;
-        rotate8(smem + row * QSTRIDE, 32 * c + 8 * (ln >> 4), vis ? dl : 0, lo, hi);
+        rotate8(qrows + row * QSTRIDE, 32 * c + 8 * (ln >> 4), vis ? dl : 0, lo, hi);
       }
       QOp *dst = qt + ((size_t)(sl * RT + rt) * NC + c) * 64 + ln;
       dst[0] = vis ? F::make_q(lo) : F::zero_q();
@@ -574,9 +658,14 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
 #pragma unroll
           for (int c = 0; c < NC / 2; ++c) {
             float lo[8], hi[8];
-            rotate8(smem + (rt * 16 + col) * QSTRIDE, 32 * c + 8 * grp, dl < 0 ? 0 : dl, lo, hi);
-            qop_wave[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
-            qop_wave[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+            rotate8(qrows + (rt * 16 + col) * QSTRIDE, 32 * c + 8 * grp, dl < 0 ? 0 : dl, lo, hi);
+            if constexpr (LDSST) {
+              qreg[rt][c] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
+              qreg[rt][c + NC / 2] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+            } else {
+              qop_wave[(rt * NC + c) * 64 + lane] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
+              qop_wave[(rt * NC + c + NC / 2) * 64 + lane] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+            }
             // one chunk at a time: keeps the rotation's temporaries from crowding out the
             // accumulators and the stage in flight
             __builtin_amdgcn_sched_barrier(0);
@@ -595,7 +684,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       for (int hh = 0; hh < 2; ++hh) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = sg.f.score(c, hh, qs[(rt * NC + c) * 64], acc);
+        for (int c = 0; c < NC; ++c)
+          acc = sg.f.score(c, hh, LDSST ? qreg[rt][c] : qs[(rt * NC + c) * 64], acc);
         sc[rt][hh] = acc;
       }
 
@@ -657,18 +747,56 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
   };
 
-  if constexpr (!COOP) {
+  if constexpr (LDSST) {
+    // Group 0 is in registers; group 1 streams into the stage now (after the barrier above:
+    // a barrier waits for outstanding LDS fills). Group i >= 1 is read from the stage, the
+    // fill of group i+1 issued, then group i computed. The compiler does not order stage
+    // reads after fills or count fills in its waits, so the waits are explicit: a fill is
+    // the only vector load in flight when the stage is read (vmcnt(0) waits for exactly it),
+    // and the stage read completes before the refill. Group 0 is computed outside the loop
+    // so that no loop iteration carries its register loads (whose waits would then drain
+    // the stage in flight).
+    if (wcount > 1) {
+      const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
+      F::load_lds(kl + gb, vl + gb, lane, stage);
+    }
+    if (wcount > 0) process(st, 0, dl_cur);
+    for (long long i = 1; i < wcount; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // group i's fill has landed
+      st.f.stage_read(stage, lane);
+      st.desc_x = next.x;
+      st.desc_y = next.y;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage read before it is refilled
+      if (i + 1 < wcount) {
+        const size_t gb = ((size_t)next2.x + head_groups) * (size_t)(32 * D);
+        F::load_lds(kl + gb, vl + gb, lane, stage);
+      }
+      next = next2;
+      ow = ow_next;
+      ow_next = ow_next2;
+      wide_rows(dl_cur, ow);
+      next2 = desc_at(min(wfirst + i + 2, wlast), ow_next2);
+      process(st, 0, dl_cur);
+    }
+  } else if constexpr (!COOP) {
     // Group i: its descriptor and offsets came with group i-1; group i+1's descriptor is
     // in and group i+2's on its way.
     for (long long i = 0; i < wcount; ++i) {
       if (i > 0) {
         desc = next;
         next = next2;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) dl_cur[rt] = dl_next[rt];
         fetch_group(st, desc, kl, vl, head_groups, lane);
-        fetch_delta(dl_next, next.y >> 8, a, row_w);
-        next2 = load_desc(a.groups, min(wfirst + i + 2, wlast));
+        if constexpr (WIDE) {
+          ow = ow_next;
+          ow_next = ow_next2;
+          wide_rows(dl_cur, ow);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) dl_cur[rt] = dl_next[rt];
+          fetch_delta(dl_next, next.y >> 8, a, row_w);
+        }
+        next2 = desc_at(min(wfirst + i + 2, wlast), ow_next2);
       }
       process(st, 0, dl_cur);
     }
@@ -704,6 +832,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // over the waves in a fixed order ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
+  if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no fill in flight
   __syncthreads();  // every wave is done with the staged queries and operands
   if (grp == 0) {
 #pragma unroll
@@ -861,10 +990,13 @@ template <int D>
 static void launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
                                hipEvent_t e1) {
   const dim3 b8(8 * 64), b4(4 * 64);
-  if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2>), grid, b4, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2>), grid, b4, 0, s, e0, e1, 0, a);
+  const bool wide = a.desc_stride == kWideStride;
+  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, true>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, true>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false>), grid, b4, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false>), grid, b4, 0, s, e0, e1, 0, a);
 }
 
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
@@ -877,10 +1009,15 @@ hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row
     if (head_dim == 128) launch_decode_bf16<128>(rt, a, grid, s, ev_start, ev_stop);
     else launch_decode_bf16<64>(rt, a, grid, s, ev_start, ev_stop);
   } else {   // fp32 pools: one 16-row tile per workgroup
-    if (head_dim == 128)
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+    const bool wide = a.desc_stride == kWideStride;
+    if (head_dim == 128 && wide)
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1, true>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+    else if (head_dim == 128)
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1, false>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+    else if (wide)
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1, true>), grid, block, 0, s, ev_start, ev_stop, 0, a);
     else
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1, false>), grid, block, 0, s, ev_start, ev_stop, 0, a);
   }
   return hipGetLastError();
 }

@@ -70,7 +70,7 @@ def test_workspace_size_formula(ctx):
     max_groups = 16 * (64 // 32)
     rows = 4 * 4
     expect = al(max_pos * half * 8) + al(half * 8)
-    expect += al(al(16 * 4 * 4) + al(max_groups * 8))
+    expect += al(al(16 * 4 * 4) + al(max_groups * 8 * 4))   # up to 8 ints per group descriptor
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
     assert H.hw_workspace_bytes(ctx) == expect
