@@ -69,6 +69,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB copy kernel (counter calibration)")
     ap.add_argument("--splits", type=int, default=0, help="force KV partitions per head")
+    ap.add_argument("--layout", default="combined",
+                    choices=["combined", "stepwise", "contiguous", "nosync"],
+                    help="cache layout the views follow (combined: the method's own)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -117,7 +120,7 @@ def main() -> int:
             kt = torch.from_numpy(k).to(dev).to(kv_dt)
             vt = torch.from_numpy(v).to(dev).to(kv_dt)
             cache.append(layer, blocks, [wl.lengths[b] for b in blocks], kt, vt)
-    cache.set_views(wl.views())
+    cache.set_views(wl.views(args.layout))
     if args.splits:
         H.hw_set_split(cache.ctx, args.splits)
     n_q_steps = total_steps if grows else 1
@@ -196,7 +199,7 @@ def main() -> int:
     cache.close()
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.layout)
     traffic = read_traffic(wl.name)
 
     line = {
@@ -205,7 +208,8 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
         "config": {
-            "workload": wl.name, "workers": n, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+            "workload": wl.name, "layout": args.layout, "workers": n, "q_heads": hq,
+            "kv_heads": hkv, "head_dim": d,
             "layers": L, "tokens_per_layer": round(avg_tokens, 1), "kv_dtype": wl.kv_dtype,
             "page_size": wl.page_size, "splits_per_head": n_splits,
             "step_ideal_bytes": int(step_bytes), "step_GBps": round(step_gbps, 1),
@@ -257,7 +261,7 @@ def stream_ceiling(torch, H, dev, sizes, reps=10):
     return {"kernel": "stream_read_kernel via hw_debug_stream_read", "points": points}
 
 
-def cpu_baseline(wl, target_s: float):
+def cpu_baseline(wl, target_s: float, layout: str = "combined"):
     """The fp64 oracle, as it stands, on the host cores: whole layers of the workload
     (all workers, all query heads) until about target_s seconds have passed, with numpy's
     BLAS on every core this process may use; then one layer on one thread."""
@@ -285,7 +289,7 @@ def cpu_baseline(wl, target_s: float):
         for layer in range(wl.n_layers):
             blocks, q = layer_inputs(layer)
             t0 = time.perf_counter()
-            O.concurrent_attention(q, blocks, wl.views(), theta=wl.theta)
+            O.concurrent_attention(q, blocks, wl.views(layout), theta=wl.theta)
             t_sum += time.perf_counter() - t0
             done += 1
             if t_sum >= target_s:
@@ -293,7 +297,7 @@ def cpu_baseline(wl, target_s: float):
     with threadpool_limits(limits=1):
         blocks, q = layer_inputs(0)
         t0 = time.perf_counter()
-        O.concurrent_attention(q, blocks, wl.views(), theta=wl.theta)
+        O.concurrent_attention(q, blocks, wl.views(layout), theta=wl.theta)
         one = time.perf_counter() - t0
     per_layer = t_sum / done
     rate = wl.n_workers / (per_layer * wl.n_layers)

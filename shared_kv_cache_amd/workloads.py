@@ -68,11 +68,43 @@ class Workload:
     def group(self) -> int:
         return self.n_q_heads // self.n_kv_heads
 
-    def views(self) -> List[List[int]]:
+    def views(self, layout: str = "combined") -> List[List[int]]:
+        """Every worker's view (block order) under one of the cache layouts the paper
+        summary (gentlecold.top) compares in s6 and whose synchronisation levels s10
+        contrasts:
+
+        combined    the method's own: the common history (prompt, then finished steps in
+                    history order), the other workers' unfinished steps in ascending
+                    worker ID, the worker's own unfinished step last.
+        stepwise    ("interleaved" / step-wise): only finished steps enter the history;
+                    other workers' unfinished steps are not visible.
+        contiguous  each worker's output kept in one contiguous span: the prompt, then
+                    every other worker's finished steps and unfinished step in ascending
+                    worker ID, the worker's own span last.
+        nosync      no synchronisation: the prompt, the worker's own finished steps and
+                    its unfinished step.
+
+        The prompt is every history block without an owner (owner -1).
+        """
+        prompt = [b for b in self.history if self.owners.get(b, -1) < 0]
+        own_done = lambda u: [b for b in self.history if self.owners.get(b, -1) == u]
         out = []
         for w in range(self.n_workers):
-            others = [self.inprogress[u] for u in range(self.n_workers) if u != w]
-            out.append(list(self.history) + others + [self.inprogress[w]])
+            others = [u for u in range(self.n_workers) if u != w]
+            if layout == "combined":
+                v = list(self.history) + [self.inprogress[u] for u in others]
+            elif layout == "stepwise":
+                v = list(self.history)
+            elif layout == "contiguous":
+                v = list(prompt)
+                for u in others:
+                    v += own_done(u) + [self.inprogress[u]]
+                v += own_done(w)
+            elif layout == "nosync":
+                v = list(prompt) + own_done(w)
+            else:
+                raise ValueError(layout)
+            out.append(v + [self.inprogress[w]])
         return out
 
     def blocks(self) -> List[int]:

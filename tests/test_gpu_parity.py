@@ -15,7 +15,7 @@ from oracle import hogwild_oracle as O
 from shared_kv_cache_amd import hogwild as H
 from shared_kv_cache_amd import workloads as W
 
-from hw_testlib import (decode_np, fill_layer, k_pool_token, kv_tensor, make_cache, max_row_rel,
+from hw_testlib import (DEV, decode_np, fill_layer, k_pool_token, kv_tensor, make_cache, max_row_rel,
                         oracle_blocks, rel_l2, v_pool_token)
 
 pytestmark = pytest.mark.gpu
@@ -230,6 +230,141 @@ def test_every_bf16_kernel_variant(head_dim, n_workers, group):
         _say(f"{wl.name} splits {splits}: rel_l2 {err:.3e}")
         assert err <= TOL["bf16"]
         assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+    cache.close()
+
+
+def _layout_workload(n_workers, n_q_heads, seed):
+    """bf16, 8 KV heads x 128: a 600-token prompt, ten paragraphs of U{40..200} tokens owned
+    round-robin (the shape of the w4_16k history, shortened) and unfinished steps of
+    U{1..150} tokens, 64-token pages."""
+    base = W.make("w4_16k", n_layers=1)
+    rng = np.random.default_rng(seed)
+    paras = [int(x) for x in rng.integers(40, 201, size=10)]
+    cur = [int(x) for x in rng.integers(1, 151, size=n_workers)]
+    history = list(range(11))
+    inprog = [11 + w for w in range(n_workers)]
+    lengths = {0: 600, **{1 + i: n for i, n in enumerate(paras)}, **{b: n for b, n in zip(inprog, cur)}}
+    owners = {0: -1, **{1 + i: i % n_workers for i in range(10)}, **{b: w for w, b in enumerate(inprog)}}
+    pages = sum(-(-n // 64) for n in lengths.values()) + 4
+    return W.Workload(**{**base.__dict__, "name": f"layouts_{n_workers}w", "seed": seed,
+                         "n_workers": n_workers, "n_q_heads": n_q_heads, "n_kv_heads": 8,
+                         "page_size": 64, "history": history, "inprogress": inprog,
+                         "lengths": lengths, "owners": owners, "n_pages": pages,
+                         "max_position": 4096})
+
+
+@pytest.mark.parametrize("n_workers,n_q_heads", [(4, 40), (8, 64)])
+def test_cache_layouts_as_views(n_workers, n_q_heads):
+    # The layouts the paper summary compares (s6 table; s10 sync levels) are block orders
+    # over the same stored blocks: combined (the method), step-wise (other workers'
+    # unfinished steps invisible, so rows of one tile differ in visibility), contiguous
+    # (each worker's output one span) and no-sync. 20 rows per KV head run the 8-wave
+    # kernels, 64 rows the cooperative ones; each layout under automatic and forced splits.
+    wl = _layout_workload(n_workers, n_q_heads, seed=11 + n_workers)
+    cache = make_cache(wl, max_splits=64)
+    fill_layer(cache, wl, 0)
+    q = wl.q(0)
+    blocks = oracle_blocks(wl, 0)
+    for layout in ("combined", "stepwise", "contiguous", "nosync"):
+        views = wl.views(layout)
+        ref, ref_lse = O.concurrent_attention(q.astype(np.float64), blocks, views, theta=wl.theta)
+        cache.set_views(views)
+        for splits in (0, 1, 7):
+            H.hw_set_split(cache.ctx, splits)
+            out, lse = decode_np(cache, 0, q)
+            err = rel_l2(out, ref)
+            _say(f"{wl.name} {layout} splits {splits}: rel_l2 {err:.3e}")
+            assert err <= TOL["bf16"]
+            assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+    cache.close()
+
+
+def test_step_commit_flow_with_block_reuse():
+    # Steps of a run (paper summary s8): every worker appends its token, the views are
+    # rebuilt, attention runs. At step 3 worker 1's step is committed: its block moves to
+    # the end of the common history and the worker continues in block 20, whose earlier
+    # contents were freed with hw_reset_block (its pages return to the free list and are
+    # handed out again); at step 5 worker 3 commits into the fresh block 21. Each step is
+    # checked against the oracle over the blocks' current contents.
+    wl = _layout_workload(4, 40, seed=23)
+    cache = make_cache(wl, max_blocks=32, n_pages=wl.n_pages + 16)
+    fill_layer(cache, wl, 0)
+    host = {b: [list(x) for x in wl.kv(0, b)] for b in wl.blocks()}   # b -> [K rows, V rows]
+    scratch_k, scratch_v = wl.kv(0, wl.history[1])                   # fill block 20, unused
+    cache.append(0, [20], [len(scratch_k)], kv_tensor(scratch_k, "bf16"), kv_tensor(scratch_v, "bf16"))
+    hist, cur = list(wl.history), list(wl.inprogress)
+    for step in range(1, 7):
+        if step == 3:
+            free0 = H.hw_free_pages(cache.ctx)
+            H.hw_reset_block(cache.ctx, 20)
+            assert H.hw_free_pages(cache.ctx) == free0 + -(-len(scratch_k) // wl.page_size)
+            hist, cur = O.commit_step_views(hist, cur, 1, 20)
+            host[20] = [[], []]
+        if step == 5:
+            hist, cur = O.commit_step_views(hist, cur, 3, 21)
+            host[21] = [[], []]
+        k, v = wl.step_kv(0, step)
+        cache.append(0, cur, [1] * 4, kv_tensor(k, "bf16"), kv_tensor(v, "bf16"))
+        for w, b in enumerate(cur):
+            host[b][0].append(k[w])
+            host[b][1].append(v[w])
+        views = [hist + [cur[u] for u in range(4) if u != w] + [cur[w]] for w in range(4)]
+        cache.set_views(views)
+        blocks = {b: (np.asarray(kk, np.float64), np.asarray(vv, np.float64))
+                  for b, (kk, vv) in host.items() if any(b in vw for vw in views)}
+        q = wl.q(0, step)
+        ref, ref_lse = O.concurrent_attention(q.astype(np.float64), blocks, views, theta=wl.theta)
+        out, lse = decode_np(cache, 0, q)
+        err = rel_l2(out, ref)
+        _say(f"commit flow step {step}: history {len(hist)} blocks, rel_l2 {err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+    cache.close()
+
+
+def test_decode_step_graph_replays_equal_eager():
+    # A whole decode step (every layer) captured as one HIP graph: kernels only once the
+    # views' tables are uploaded (no memset nodes). Each replay, with eager work and
+    # synchronisations in between, must equal the eager step bit for bit.
+    wl = _layout_workload(4, 40, seed=31)
+    wl = W.Workload(**{**wl.__dict__, "n_layers": 4})
+    cache = make_cache(wl)
+    for layer in range(4):
+        fill_layer(cache, wl, layer)
+    cache.set_views(wl.views())
+    qs = [torch.from_numpy(wl.q(layer)).to(DEV) for layer in range(4)]
+    outs = [torch.empty_like(q) for q in qs]
+    lses = [torch.empty(q.shape[:2], device=DEV) for q in qs]
+
+    def step():
+        for layer in range(4):
+            cache.decode(layer, qs[layer], out=outs[layer], lse=lses[layer])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs], [x.clone() for x in lses]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer in range(4):
+            assert torch.equal(outs[layer], eager[0][layer]), (rep, layer)
+            assert torch.equal(lses[layer], eager[1][layer]), (rep, layer)
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+    _say("graph replays equal the eager step")
     cache.close()
 
 

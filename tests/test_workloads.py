@@ -64,3 +64,48 @@ def test_sink_keys_scaled():
     np.testing.assert_array_equal(k[:4, 7], W.round_to_bf16_values(raw[:4, 7] * 8))
     np.testing.assert_array_equal(k[4:, 7], W.round_to_bf16_values(raw[4:, 7]))
     np.testing.assert_array_equal(k[:, :7], W.round_to_bf16_values(raw[:, :7]))
+
+
+def _two_worker_structure():
+    """Prompt P, finished steps A1 (worker 0), B1 (worker 1), A2 (worker 0) in history order;
+    unfinished steps A3 (worker 0) and B2 (worker 1). Ids 0..6 = P A1 B1 A2 A3 B2."""
+    base = W.make("tiny_fp32")
+    P, A1, B1, A2, A3, B2 = range(6)
+    lengths = {b: 8 for b in range(6)}
+    owners = {P: -1, A1: 0, B1: 1, A2: 0, A3: 0, B2: 1}
+    wl = W.Workload(**{**base.__dict__, "history": [P, A1, B1, A2], "inprogress": [A3, B2],
+                       "lengths": lengths, "owners": owners})
+    return wl, (P, A1, B1, A2, A3, B2)
+
+
+def test_layout_views_printed_orders():
+    # gentlecold.top summary s6 (combined layout; layout table) and s10 (no sync / step-wise /
+    # token-wise): the views written out by hand for a two-worker history
+    wl, (P, A1, B1, A2, A3, B2) = _two_worker_structure()
+    assert wl.views("combined") == [[P, A1, B1, A2, B2, A3], [P, A1, B1, A2, A3, B2]]
+    assert wl.views("stepwise") == [[P, A1, B1, A2, A3], [P, A1, B1, A2, B2]]
+    assert wl.views("contiguous") == [[P, B1, B2, A1, A2, A3], [P, A1, A2, A3, B1, B2]]
+    assert wl.views("nosync") == [[P, A1, A2, A3], [P, B1, B2]]
+    assert wl.views() == wl.views("combined")
+    with pytest.raises(ValueError):
+        wl.views("token")
+
+
+@pytest.mark.parametrize("name", ["w4_16k", "w8_32k", "tiny_fp32"])
+def test_layout_views_properties(name):
+    wl = W.make(name, n_layers=1)
+    comb = wl.views("combined")
+    for layout in ("combined", "stepwise", "contiguous", "nosync"):
+        for w, v in enumerate(wl.views(layout)):
+            assert len(v) == len(set(v)) and v[-1] == wl.inprogress[w]
+            if layout == "contiguous":
+                assert sorted(v) == sorted(comb[w])           # same blocks, other order
+            if layout in ("stepwise", "nosync"):
+                assert set(v) <= set(comb[w])
+                assert not set(v) & {wl.inprogress[u] for u in range(wl.n_workers) if u != w}
+            if layout == "nosync":
+                assert all(wl.owners.get(b, -1) in (-1, w) for b in v)
+            if layout == "contiguous":   # each worker's blocks form one span
+                owner_seq = [wl.owners.get(b, -1) for b in v]
+                spans = [o for i, o in enumerate(owner_seq) if i == 0 or o != owner_seq[i - 1]]
+                assert len(spans) == len(set(spans))
