@@ -170,15 +170,21 @@ def concurrent_attention(q: np.ndarray,
                          heads: Optional[Sequence[int]] = None):
     """Exact concurrent attention for one decode step of one layer.
 
-    q       [N, Hq, D] raw (unrotated) queries, one token per worker.
+    q       [N, Hq, D] raw (unrotated) queries, one token per worker; or
+            [N, n_new, Hq, D]: n_new tokens per worker processed together (a
+            paragraph header inserted into a fresh block, [P1] s8 step 4). Token t
+            sits at position q_pos - (n_new - 1 - t) and attends to the keys at or
+            before its own position only (causal), so the last token is the one-token
+            case and earlier tokens do not see the ones after them.
     blocks  block id -> (K [len, Hkv, D], V [len, Hkv, D]) raw, unrotated.
     views   per worker, block ids in view order.
     offsets per worker, start position of each view block (None: running sum).
     q_pos   per worker, query position (None: last token of the view).
     heads   query heads to compute (None: all); others stay NaN.
 
-    Returns (out [N, Hq, D], lse [N, Hq]) in fp64; lse is the natural-log
-    normaliser log(sum_t exp(s_t)).
+    Returns (out [N, Hq, D], lse [N, Hq]) in fp64 (with n_new: [N, n_new, Hq, D] and
+    [N, n_new, Hq]); lse is the natural-log normaliser log(sum_t exp(s_t)). A token
+    with no key at or before it gets out = 0 and lse = -inf.
 
     Steps ([P1] s5, s8): concatenate the view's keys and values; give token j
     of a block at offset o the true position o + j; rho every key at its true
@@ -186,23 +192,42 @@ def concurrent_attention(q: np.ndarray,
     softmax over every token of the view; out = sum_t softmax_t v_t.
     """
     q = np.asarray(q, dtype=np.float64)
-    n_workers, hq, d = q.shape
     lengths = {b: int(kv[0].shape[0]) for b, kv in blocks.items()}
+    offs, qps = _resolve(views, lengths, offsets, q_pos)
+    if q.ndim == 4:   # several tokens per worker: each token on its own, causally
+        n_new = q.shape[1]
+        outs, lses = [], []
+        for t in range(n_new):
+            back = n_new - 1 - t
+            o, l_ = _attend(q[:, t], blocks, views, lengths, offs, [p - back for p in qps],
+                            qps, theta, scale, heads, causal=True)
+            outs.append(o)
+            lses.append(l_)
+        return np.stack(outs, axis=1), np.stack(lses, axis=1)
+    return _attend(q, blocks, views, lengths, offs, qps, qps, theta, scale, heads, causal=False)
+
+
+def _attend(q, blocks, views, lengths, offs, qps, last_qps, theta, scale, heads, causal):
+    """One query token per worker, at qps[w], over the worker's view (validated against
+    last_qps[w], the position of the worker's last query token). causal: keys after the
+    token are left out."""
+    n_workers, hq, d = q.shape
     hkv = next(iter(blocks.values()))[0].shape[1]
     if hq % hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     group = hq // hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    offs, qps = _resolve(views, lengths, offsets, q_pos)
     heads = list(range(hq)) if heads is None else list(heads)
     out = np.full((n_workers, hq, d), np.nan)
     lse = np.full((n_workers, hq), np.nan)
     for w in range(n_workers):
         view = list(views[w])
-        err = view_error(view, offs[w], lengths, qps[w])
+        err = view_error(view, offs[w], lengths, last_qps[w])
         if err:
             raise ValueError(f"worker {w}: {err}")
+        if qps[w] < 0:
+            raise ValueError(f"worker {w}: query position below 0")
         if sum(lengths[b] for b in view) == 0:
             out[w, heads] = 0.0
             lse[w, heads] = -np.inf
@@ -210,6 +235,13 @@ def concurrent_attention(q: np.ndarray,
         pos = np.concatenate([o + np.arange(lengths[b]) for b, o in zip(view, offs[w])])
         keys = np.concatenate([np.asarray(blocks[b][0], np.float64) for b in view])
         vals = np.concatenate([np.asarray(blocks[b][1], np.float64) for b in view])
+        if causal:
+            keep = pos <= qps[w]
+            pos, keys, vals = pos[keep], keys[keep], vals[keep]
+            if len(pos) == 0:
+                out[w, heads] = 0.0
+                lse[w, heads] = -np.inf
+                continue
         q_rot = rope(q[w], qps[w], theta)
         for kvh in sorted({h // group for h in heads}):
             k_rot = rope(keys[:, kvh, :], pos, theta)

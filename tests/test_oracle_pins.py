@@ -384,3 +384,96 @@ def test_planted_oracle_mistakes_fail_a_pin(monkeypatch, target, mutant):
     assert _pin_suite() == []
     monkeypatch.setattr(O, target, mutant)
     assert _pin_suite() != [], f"mutant {mutant.__name__} of {target} passed every pin"
+
+
+# ------------------------------------------- several query tokens per worker
+
+def _truncated_case(q_tok, blocks, views, offsets, pos):
+    """The one-token problem of a token at position pos[w]: every block of every view cut
+    down to its keys at or before pos[w] (new block ids, explicit offsets kept)."""
+    new_blocks, new_views, new_offs = {}, [], []
+    for w, view in enumerate(views):
+        v2, o2 = [], []
+        for b, off in zip(view, offsets[w]):
+            k, v = blocks[b]
+            keep = max(0, min(len(k), pos[w] - off + 1))
+            nb = (w, b)
+            new_blocks[nb] = (k[:keep], v[:keep])
+            v2.append(nb)
+            o2.append(off)
+        new_views.append(v2)
+        new_offs.append(o2)
+    return new_blocks, new_views, new_offs
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_several_tokens_equal_one_token_problems_cut_at_each_token(seed):
+    # [P1] s8 step 4: a fresh block starts with a paragraph header, several tokens
+    # processed at once. Token t (position q_pos - (n_new - 1 - t)) must equal the
+    # one-token oracle over the views cut at its position: a different code path (cut
+    # blocks instead of a mask), so a wrong shift, sign or mask edge fails here.
+    rng = np.random.default_rng(500 + seed)
+    q1, blocks, views, _ = _rand_case(rng, n_workers=3)
+    n_new = 1 + seed
+    # grow each worker's own (last) block so that it holds the n_new tokens
+    for w, view in enumerate(views):
+        b = view[-1]
+        k, v = blocks[b]
+        extra = max(0, n_new - len(k))
+        if extra:
+            blocks[b] = (np.concatenate([k, rng.standard_normal((extra,) + k.shape[1:])]),
+                         np.concatenate([v, rng.standard_normal((extra,) + v.shape[1:])]))
+    lengths = {b: len(kv[0]) for b, kv in blocks.items()}
+    offsets = []
+    for v in views:   # running sums, with random gaps for odd seeds
+        off, acc = [], int(rng.integers(0, 3)) if seed % 2 else 0
+        for b in v:
+            off.append(acc)
+            acc += lengths[b] + (int(rng.integers(0, 4)) if seed % 2 else 0)
+        offsets.append(off)
+    q = rng.standard_normal((3, n_new) + q1.shape[1:])
+    out, lse = O.concurrent_attention(q, blocks, views, offsets=offsets)
+    assert out.shape == q.shape and lse.shape == q.shape[:3]
+    qps = [offsets[w][-1] + lengths[v[-1]] - 1 for w, v in enumerate(views)]
+    for t in range(n_new):
+        pos = [p - (n_new - 1 - t) for p in qps]
+        nb, nv, no = _truncated_case(q[:, t], blocks, views, offsets, pos)
+        ref, ref_lse = O.concurrent_attention(q[:, t], nb, nv, offsets=no, q_pos=pos)
+        assert np.array_equal(out[:, t], ref), t
+        assert np.array_equal(lse[:, t], ref_lse), t
+
+
+def test_several_tokens_one_token_case_and_interleaved_keys():
+    rng = np.random.default_rng(77)
+    q1, blocks, views, offsets = _rand_case(rng, n_workers=2)
+    out1, lse1 = O.concurrent_attention(q1, blocks, views, offsets=offsets)
+    out, lse = O.concurrent_attention(q1[:, None], blocks, views, offsets=offsets)
+    assert np.array_equal(out[:, 0], out1) and np.array_equal(lse[:, 0], lse1)
+
+    # Keys between the query tokens: with an explicit q_pos the tokens need not be stored
+    # keys. Worker 0's block 5 holds positions 100..106, block 7 holds 107..108 and the
+    # queries sit at 107, 108, 109: the token at 107 sees block 7's first key only, the one
+    # at 109 sees both. Written out by hand.
+    d, hkv = 8, 1
+    k_own, v_own = rng.standard_normal((7, hkv, d)), rng.standard_normal((7, hkv, d))
+    k7, v7 = rng.standard_normal((2, hkv, d)), rng.standard_normal((2, hkv, d))
+    qq = rng.standard_normal((1, 3, 1, d))
+    bl = {5: (k_own, v_own), 7: (k7, v7)}
+    out, lse = O.concurrent_attention(qq, bl, [[5, 7]], offsets=[[100, 107]], q_pos=[109])
+    for t, p in enumerate((107, 108, 109)):
+        n7 = min(2, p - 107 + 1)
+        keys = np.concatenate([k_own, k7[:n7]])
+        vals = np.concatenate([v_own, v7[:n7]])
+        kpos = np.concatenate([100 + np.arange(7), 107 + np.arange(n7)])
+        s = O.rope(keys[:, 0], kpos, 1e4) @ O.rope(qq[0, t], p, 1e4)[0] / math.sqrt(d)
+        w_ = np.exp(s - s.max())
+        assert _rel(out[0, t, 0], (w_ @ vals[:, 0]) / w_.sum()) <= 1e-12
+        assert abs(lse[0, t, 0] - (s.max() + math.log(w_.sum()))) <= 1e-12
+
+    # a token with no key at or before it: out 0, lse -inf
+    out, lse = O.concurrent_attention(qq, {7: (k7, v7)}, [[7]], offsets=[[107]], q_pos=[108])
+    assert np.all(out[0, 0] == 0) and lse[0, 0, 0] == -np.inf   # the token at 106
+    assert np.isfinite(lse[0, 1:]).all()
+    with pytest.raises(ValueError):   # a query position below 0
+        O.concurrent_attention(rng.standard_normal((1, 3, 1, d)), {7: (k7[:1], v7[:1])}, [[7]],
+                               offsets=[[0]], q_pos=[1])
