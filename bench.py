@@ -4,6 +4,9 @@
 A step is one decode step of every worker over every layer the workload times
 (for w8_32k each layer first appends one new token per worker). Inputs are
 seeded synthetic tensors already resident in HBM when the timed region starts.
+With --query-tokens K > 1 every worker queries K tokens per step together
+(hw_concurrent_decode_tokens: a paragraph header's tokens, causal), over the
+same cache.
 
 Prints ONE JSON line: worker-steps/s (value), the step's ideal-bytes GB/s,
 a roofline object for the dominant kernel (concurrent_decode: algorithmic
@@ -72,11 +75,17 @@ def main() -> int:
     ap.add_argument("--layout", default="combined",
                     choices=["combined", "stepwise", "contiguous", "nosync"],
                     help="cache layout the views follow (combined: the method's own)")
+    ap.add_argument("--query-tokens", type=int, default=1,
+                    help="query tokens per worker and step (several: one causal decode of all)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the concurrent-"
               "attention step here is single-GPU by design", file=sys.stderr)
+        return 2
+
+    if args.query_tokens < 1:
+        print("--query-tokens must be at least 1", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -108,7 +117,8 @@ def main() -> int:
         n_layers=L, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, page_size=wl.page_size,
         n_pages=wl.n_pages, max_blocks=len(wl.blocks()) + 1, max_workers=n,
         max_position=wl.max_position, kv_dtype=wl.kv_dtype, page_seed=wl.page_seed,
-        rope_theta=wl.theta, max_splits=512 if args.splits > 256 else 0, device="cuda:0")
+        rope_theta=wl.theta, max_splits=512 if args.splits > 256 else 0,
+        max_query_tokens=args.query_tokens, device="cuda:0")
     blocks = wl.blocks()
 
     def gen(layer):
@@ -123,15 +133,20 @@ def main() -> int:
     cache.set_views(wl.views(args.layout))
     if args.splits:
         H.hw_set_split(cache.ctx, args.splits)
-    n_q_steps = total_steps if grows else 1
-    q_dev = [[torch.from_numpy(wl.q(layer, s if grows else 0)).to(dev) for s in range(n_q_steps)]
+    kq = args.query_tokens
+    n_q_steps = total_steps if grows and kq == 1 else 1
+
+    def q_host(layer, s):
+        return wl.q(layer, s) if kq == 1 else wl.q_tokens(layer, kq)
+
+    q_dev = [[torch.from_numpy(q_host(layer, s if grows else 0)).to(dev) for s in range(n_q_steps)]
              for layer in range(L)]
     step_kv = None
     if grows:   # one new token per worker per layer per step, pre-staged in HBM
         step_kv = [[tuple(torch.from_numpy(x).to(dev).to(kv_dt) for x in wl.step_kv(layer, s + 1))
                     for s in range(total_steps)] for layer in range(L)]
-    outs = [torch.empty((n, hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
-    lses = [torch.empty((n, hq), dtype=torch.float32, device=dev) for _ in range(L)]
+    outs = [torch.empty((n, kq, hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    lses = [torch.empty((n, kq, hq), dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s: {wl.name}, {L} layers, T={wl.total_tokens()}")
 
@@ -145,9 +160,13 @@ def main() -> int:
                 k, v = step_kv[layer][s]
                 H.hw_append_kv(cache.ctx, layer, wl.inprogress, [1] * n, k.data_ptr(),
                                v.data_ptr(), stream)
-            q = q_dev[layer][s if grows else 0]
-            H.hw_concurrent_decode(cache.ctx, layer, q.data_ptr(), outs[layer].data_ptr(),
-                                   lses[layer].data_ptr(), stream)
+            q = q_dev[layer][s if n_q_steps > 1 else 0]
+            if kq == 1:
+                H.hw_concurrent_decode(cache.ctx, layer, q.data_ptr(), outs[layer].data_ptr(),
+                                       lses[layer].data_ptr(), stream)
+            else:
+                H.hw_concurrent_decode_tokens(cache.ctx, layer, kq, q.data_ptr(),
+                                              outs[layer].data_ptr(), lses[layer].data_ptr(), stream)
         state["step"] = s + 1
 
     def tokens_now():
@@ -185,7 +204,7 @@ def main() -> int:
     # plus q read and out / lse written.
     avg_tokens = 0.5 * (t_tok0 + t_tok1) if grows else float(wl.total_tokens())
     kv_bytes = avg_tokens * hkv * d * 2 * elem
-    io_bytes = n * hq * d * 4 * 2 + n * hq * 4
+    io_bytes = n * kq * (hq * d * 4 * 2 + hq * 4)
     launch_bytes = kv_bytes + io_bytes
     append_bytes = (n * hkv * d * elem * 2 * 2) if grows else 0   # read + write new K and V
     step_bytes = L * (launch_bytes + append_bytes)
@@ -199,7 +218,7 @@ def main() -> int:
     cache.close()
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, args.layout)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.layout, kq)
     traffic = read_traffic(wl.name)
 
     line = {
@@ -215,7 +234,7 @@ def main() -> int:
             "step_ideal_bytes": int(step_bytes), "step_GBps": round(step_gbps, 1),
             "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
             "decode_kernel_us": round(dec_avg * 1e3, 3),
-            "appends_per_step": L if grows else 0,
+            "appends_per_step": L if grows else 0, "query_tokens": kq,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -261,7 +280,7 @@ def stream_ceiling(torch, H, dev, sizes, reps=10):
     return {"kernel": "stream_read_kernel via hw_debug_stream_read", "points": points}
 
 
-def cpu_baseline(wl, target_s: float, layout: str = "combined"):
+def cpu_baseline(wl, target_s: float, layout: str = "combined", query_tokens: int = 1):
     """The fp64 oracle, as it stands, on the host cores: whole layers of the workload
     (all workers, all query heads) until about target_s seconds have passed, with numpy's
     BLAS on every core this process may use; then one layer on one thread."""
@@ -282,7 +301,8 @@ def cpu_baseline(wl, target_s: float, layout: str = "combined"):
 
     def layer_inputs(layer):
         blocks = {b: tuple(x.astype(np.float64) for x in wl.kv(layer, b)) for b in wl.blocks()}
-        return blocks, wl.q(layer).astype(np.float64)
+        q = wl.q(layer) if query_tokens == 1 else wl.q_tokens(layer, query_tokens)
+        return blocks, q.astype(np.float64)
 
     done, t_sum = 0, 0.0
     with threadpool_limits(limits=threads):
@@ -304,7 +324,8 @@ def cpu_baseline(wl, target_s: float, layout: str = "combined"):
     log(f"cpu oracle: {done} layers in {t_sum:.2f}s on {threads} threads -> {rate:.4f} "
         f"worker-steps/s; one layer on 1 thread {one:.2f}s")
     return {"value": round(rate, 5), "unit": "worker-steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {wl.n_layers} layers at step 0, all {wl.n_workers} workers and "
+            "sample": f"{done} of {wl.n_layers} layers at step 0, all {wl.n_workers} workers "
+                      f"({query_tokens} query token(s) each) and "
                       f"{wl.n_q_heads} query heads; fp64 numpy oracle, BLAS on {threads} threads; "
                       f"rate = workers / (mean seconds per layer x {wl.n_layers} layers)",
             "cpu_model": model, "single_thread_s_per_layer": round(one, 3)}

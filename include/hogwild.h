@@ -71,6 +71,7 @@ typedef struct {
   int32_t max_workers;  /* most workers any view set may have */
   int32_t max_position; /* every local position and every query offset delta must be below */
   int32_t max_splits;   /* most KV partitions per head a decode may use; 0 => 256 */
+  int32_t max_query_tokens; /* most query tokens per worker of hw_concurrent_decode_tokens; 0 => 1 */
   hw_dtype kv_dtype;    /* element type of both pools */
   uint32_t page_seed;   /* 0: free pages handed out in ascending order; else shuffled (below) */
   double rope_theta;    /* RoPE base, > 1 */
@@ -159,6 +160,20 @@ hw_status hw_set_views(hw_ctx *ctx, int32_t n_workers, const int32_t *view_len,
  * a delta at or above max_position), HW_ERR_HIP. */
 hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float *out,
                                float *lse, void *stream);
+
+/* Several query tokens per worker in one pass (summary s8 step 4: a worker that starts a
+ * fresh block first inserts a paragraph header, whose tokens are appended and attended
+ * together). q: device fp32 [n_workers][n_new][n_q_heads][head_dim], raw. Token t of worker
+ * w sits at position q_pos(w) - (n_new - 1 - t), q_pos(w) being the position
+ * hw_concurrent_decode uses (the last token), and attends to the keys of w's view at or
+ * before its own position: causal, so a block's keys after the token (this step's later
+ * tokens of the worker's own block) are left out. out: device fp32, same shape as q; lse:
+ * device fp32 [n_workers][n_new][n_q_heads] or NULL. A token with no key at or before it
+ * gets out = 0 and lse = -inf. n_new = 1 computes what hw_concurrent_decode computes.
+ * Errors: as hw_concurrent_decode; HW_ERR_INVALID_ARG when n_new < 1 or n_new >
+ * max_query_tokens; HW_ERR_STALE_VIEW when a worker's first token would sit below 0. */
+hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
+                                      float *out, float *lse, void *stream);
 
 /* Return a block's pages to the free list and set its length to 0 in every layer, e.g. after
  * its step was committed and the worker starts a fresh block (summary s8). Pages are handed

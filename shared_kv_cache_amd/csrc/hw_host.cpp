@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <thread>
 #include <vector>
@@ -59,8 +60,10 @@ struct Views {
 struct Resolution {
   std::vector<int32_t> seg_blocks;
   std::vector<int32_t> delta;   // [n_seg][n_workers]
-  std::vector<int32_t> g_page, g_gip, g_seg, g_valid;
+  std::vector<int32_t> g_page, g_gip, g_seg, g_valid, g_start;   // g_start: local position
   int32_t n_workers = 0;
+  // smallest query position over the workers whose view holds a token
+  int64_t min_qpos = std::numeric_limits<int64_t>::max();
 };
 
 }  // namespace
@@ -88,6 +91,7 @@ struct hw_ctx {
   int32_t up_n_groups = 0, up_n_seg = 0, up_n_workers = 0;
   size_t up_groups_off = 0;  // byte offset of the group list inside the tables region
   int32_t up_stride = 2;     // ints per uploaded group descriptor
+  int64_t up_min_qpos = 0;   // Resolution::min_qpos of the uploaded tables
   std::vector<uint8_t> up_seg_first;   // per group: 1 if it starts a block of the union
   // partition bounds of the uploaded group list, for bounds_splits partitions at bounds_alpha
   std::vector<int32_t> bounds;
@@ -122,15 +126,16 @@ uint64_t splitmix64_next(uint64_t &state) {
   return z ^ (z >> 31);
 }
 
-int32_t rows_total(const hw_ctx *c, int32_t n_workers) {
-  return n_workers * (c->cfg.n_q_heads / c->cfg.n_kv_heads);
+// Stacked query rows of one KV head: (worker, query token, head of the KV head's group).
+int32_t rows_total(const hw_ctx *c, int32_t n_workers, int32_t n_new = 1) {
+  return n_workers * n_new * (c->cfg.n_q_heads / c->cfg.n_kv_heads);
 }
 
 void layout_workspace(hw_ctx *c) {
   const hw_config &g = c->cfg;
   const size_t half = (size_t)g.head_dim / 2;
   const size_t max_groups = (size_t)g.n_pages * (g.page_size / hw::kTokGroup);
-  const size_t max_rows = (size_t)g.max_workers * (g.n_q_heads / g.n_kv_heads);
+  const size_t max_rows = (size_t)g.max_workers * g.max_query_tokens * (g.n_q_heads / g.n_kv_heads);
   size_t off = 0;
   c->off_trig = off;
   off = align_up(off + (size_t)g.max_position * half * 2 * sizeof(float));
@@ -161,8 +166,15 @@ hw_status check_config(const hw_config *g, std::string &m) {
   if (g->max_blocks <= 0 || g->max_blocks > (1 << 22)) return m = "max_blocks out of range", HW_ERR_INVALID_ARG;
   if (g->max_workers <= 0 || g->max_workers > 1024) return m = "max_workers out of range", HW_ERR_INVALID_ARG;
   if (g->max_position <= 0) return m = "max_position must be > 0", HW_ERR_INVALID_ARG;
-  if ((int64_t)g->max_workers * (g->n_q_heads / g->n_kv_heads) >= (1 << 22))
-    return m = "max_workers * (n_q_heads / n_kv_heads) must be below 2^22", HW_ERR_INVALID_ARG;
+  if (g->max_query_tokens < 0 || g->max_query_tokens > 1024)
+    return m = "max_query_tokens must be in [0, 1024]", HW_ERR_INVALID_ARG;
+  const int64_t mqt = std::max<int64_t>(1, g->max_query_tokens);
+  if ((int64_t)g->max_workers * mqt * (g->n_q_heads / g->n_kv_heads) >= (1 << 22))
+    return m = "max_workers * max_query_tokens * (n_q_heads / n_kv_heads) must be below 2^22",
+           HW_ERR_INVALID_ARG;
+  if ((int64_t)g->max_workers * mqt * g->n_q_heads * g->head_dim >= ((int64_t)1 << 31))
+    return m = "max_workers * max_query_tokens * n_q_heads * head_dim must be below 2^31",
+           HW_ERR_INVALID_ARG;
   if (g->max_splits < 0 || g->max_splits > 65535) return m = "max_splits out of range", HW_ERR_INVALID_ARG;
   if (g->kv_dtype != HW_BF16 && g->kv_dtype != HW_F32) return m = "unknown kv_dtype", HW_ERR_INVALID_ARG;
   if (!(g->rope_theta > 1.0) || !std::isfinite(g->rope_theta)) return m = "rope_theta must be > 1", HW_ERR_INVALID_ARG;
@@ -257,9 +269,9 @@ void commit_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *id
 
 // ---- view resolution ---------------------------------------------------------------
 
-int32_t row_blocks_for(const hw_ctx *c, int32_t n_workers) {
+int32_t row_blocks_for(const hw_ctx *c, int32_t rows) {
   const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
-  return std::max(1, (rows_total(c, n_workers) + rpb - 1) / rpb);
+  return std::max(1, (rows + rpb - 1) / rpb);
 }
 
 // Cost of a partition: one per token group, plus alpha per block of the union it touches
@@ -317,8 +329,8 @@ double split_alpha(const hw_ctx *c, int32_t rows) {
   return (c->cfg.kv_dtype == HW_BF16 && first > 32) ? HW_SPLIT_ALPHA_COOP : 0.0;
 }
 
-int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
-  const int32_t row_blocks = row_blocks_for(c, n_workers);
+int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {
+  const int32_t row_blocks = row_blocks_for(c, rows);
   const int32_t per_head = c->cfg.n_kv_heads * std::max(1, row_blocks);
   // Workgroups for about three quarters of the CUs: measured on MI355X, this still keeps
   // HBM saturated while each wave takes more groups (fixed per-wave costs amortised, less
@@ -328,9 +340,9 @@ int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
   return std::max(1, std::min(s, c->cfg.max_splits));
 }
 
-int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t n_workers) {
+int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {
   return c->split_override > 0 ? std::min(c->split_override, c->cfg.max_splits)
-                               : auto_splits(c, n_groups, n_workers);
+                               : auto_splits(c, n_groups, rows);
 }
 
 // Signature of everything a resolution depends on; equal signatures => equal tables.
@@ -386,6 +398,7 @@ hw_status resolve(hw_ctx *c, int32_t layer, Resolution &r) {
         return c->fail(HW_ERR_STALE_VIEW, "worker " + std::to_string(w) +
                                               ": query offset reaches max_position");
     }
+    if (!spans.empty()) r.min_qpos = std::min(r.min_qpos, qpos[w]);
     std::sort(spans.begin(), spans.end());
     for (size_t i = 1; i < spans.size(); ++i)
       if (spans[i].first < spans[i - 1].second)
@@ -405,7 +418,6 @@ hw_status resolve(hw_ctx *c, int32_t layer, Resolution &r) {
       if (s >= 0) r.delta[(size_t)s * n + w] = (int32_t)(qpos[w] - offs[w][i]);
     }
   }
-  const int32_t gpp = g.page_size / hw::kTokGroup;
   for (int32_t s = 0; s < n_seg; ++s) {
     const BlockState &bs = c->blocks[r.seg_blocks[s]];
     const int32_t len = bs.len[layer];
@@ -414,9 +426,9 @@ hw_status resolve(hw_ctx *c, int32_t layer, Resolution &r) {
       r.g_gip.push_back((t % g.page_size) / hw::kTokGroup);
       r.g_seg.push_back(s);
       r.g_valid.push_back(std::min(hw::kTokGroup, len - t));
+      r.g_start.push_back(t);
     }
   }
-  (void)gpp;
   return HW_OK;
 }
 
@@ -476,6 +488,7 @@ hw_status hw_create(const hw_config *cfg, hw_ctx **out) {
   }
   c->cfg = *cfg;
   if (c->cfg.max_splits == 0) c->cfg.max_splits = 256;
+  if (c->cfg.max_query_tokens == 0) c->cfg.max_query_tokens = 1;
   if (c->cfg.softmax_scale == 0.0f) c->cfg.softmax_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
   c->blocks.resize(cfg->max_blocks);
   for (auto &b : c->blocks) b.len.assign(cfg->n_layers, 0);
@@ -644,20 +657,35 @@ hw_status hw_set_views(hw_ctx *ctx, int32_t n_workers, const int32_t *view_len,
   return HW_OK;
 }
 
-hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float *out, float *lse,
-                               void *stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode of n_new query tokens per worker (n_new = 1: the one-token step).
+hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q, float *out,
+                      float *lse, hipStream_t s) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   const hw_config &g = ctx->cfg;
   if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (n_new < 1 || n_new > g.max_query_tokens)
+    return ctx->fail(HW_ERR_INVALID_ARG, "n_new must be in [1, max_query_tokens]");
   if (!q || !out) return ctx->fail(HW_ERR_INVALID_ARG, "q/out NULL");
   if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
   if (!ctx->views.set) return ctx->fail(HW_ERR_STALE_VIEW, "no views set");
-  hipStream_t s = (hipStream_t)stream;
   const int32_t n = ctx->views.n_workers;
   char *tables = (char *)ctx->ws + ctx->off_tables;
+  const int32_t group = g.n_q_heads / g.n_kv_heads;
+  const int32_t rows = rows_total(ctx, n, n_new);
+  // Group descriptors: wide ones (each group's offsets beside it) for the 8-wave kernels
+  // when every worker fits and each worker has one token; with several tokens, the group's
+  // first local position beside {x, y} for the causal mask; else {x, y} alone. The
+  // cooperative kernels read the offset table per phase.
+  const bool wide = n_new == 1 && n <= hw::kWideWorkers &&
+                    hw::decode_waves(g.kv_dtype, rows) == 8 && rows <= hw::rows_per_block(g.kv_dtype);
+  const int32_t stride = wide ? hw::kWideStride : (n_new > 1 ? 4 : 2);
 
   std::vector<int64_t> sig = signature(ctx, layer);
-  if (!ctx->uploaded_valid || sig != ctx->uploaded_sig) {
+  if (!ctx->uploaded_valid || sig != ctx->uploaded_sig || ctx->up_stride != stride) {
     Resolution r;
     hw_status st = resolve(ctx, layer, r);
     if (st != HW_OK) return st;
@@ -665,12 +693,6 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     if (st != HW_OK) return st;
     const int32_t n_seg = (int32_t)r.seg_blocks.size();
     const int32_t n_groups = (int32_t)r.g_page.size();
-    // Wide descriptors (each group's offsets beside it) for the 8-wave kernels when every
-    // worker fits; the cooperative kernels read the offset table per phase instead.
-    const int32_t rows_all = n * (g.n_q_heads / g.n_kv_heads);
-    const bool wide = n <= hw::kWideWorkers && hw::decode_waves(g.kv_dtype, rows_all) == 8 &&
-                      rows_all <= hw::rows_per_block(g.kv_dtype);
-    const int32_t stride = wide ? hw::kWideStride : 2;
     const size_t delta_bytes = align_up((size_t)n_seg * n * sizeof(int32_t));
     const size_t bytes = delta_bytes + (size_t)n_groups * stride * sizeof(int32_t);
     const int slot = ctx->next_slot;
@@ -688,9 +710,13 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
       int32_t *d = gd + (size_t)stride * i;
       d[0] = r.g_page[i] * g.n_kv_heads * gpp + r.g_gip[i];
       d[1] = (r.g_seg[i] << 8) | r.g_valid[i];
-      if (wide)
+      if (wide) {
         for (int32_t k = 0; k < hw::kWideWorkers; ++k)
           d[2 + k] = k < n ? r.delta[(size_t)r.g_seg[i] * n + k] : -1;
+      } else if (stride == 4) {
+        d[2] = r.g_start[i];
+        d[3] = 0;
+      }
       ctx->up_seg_first[i] = (i == 0 || r.g_seg[i] != r.g_seg[i - 1]) ? 1 : 0;
     }
     ctx->bounds_splits = -1;
@@ -708,12 +734,14 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     ctx->up_n_workers = n;
     ctx->up_groups_off = delta_bytes;
     ctx->up_stride = stride;
+    ctx->up_min_qpos = r.min_qpos;
   }
+  // Token 0 of a worker sits n_new - 1 positions before its query position.
+  if (ctx->up_min_qpos < (int64_t)n_new - 1)
+    return ctx->fail(HW_ERR_STALE_VIEW, "a worker's first query token would sit below position 0");
 
-  const int32_t group = g.n_q_heads / g.n_kv_heads;
-  const int32_t rows = n * group;
   const int32_t n_groups = ctx->up_n_groups;
-  const int32_t splits = choose_splits(ctx, n_groups, n);
+  const int32_t splits = choose_splits(ctx, n_groups, rows);
   const size_t eb = kv_elem_bytes(ctx);
   hw::DecodeArgs a{};
   a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
@@ -736,6 +764,8 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
   a.page_groups = g.page_size / hw::kTokGroup;
   a.rows_per_block = hw::rows_per_block(g.kv_dtype);
   a.inv_group = 1.0f / (float)group;
+  a.inv_rpw = 1.0f / (float)(n_new * group);
+  a.n_new = n_new;
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
   a.desc_stride = ctx->up_stride;
   if (splits <= hw::kMaxBoundSplits) {
@@ -748,7 +778,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     }
     std::copy(ctx->bounds.begin(), ctx->bounds.end(), a.split_begin);
   }
-  const int32_t row_blocks = row_blocks_for(ctx, n);
+  const int32_t row_blocks = row_blocks_for(ctx, rows);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
   hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
   hw_status st = post_launch(ctx,
@@ -763,7 +793,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     m.part_lse = a.part_lse;
     m.out = out;
     m.lse = lse;
-    m.n_workers = n;
+    m.n_workers = n * n_new;   // query tokens, each merged on its own
     m.n_q_heads = g.n_q_heads;
     m.n_kv_heads = g.n_kv_heads;
     m.group = group;
@@ -773,6 +803,20 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
     if (st != HW_OK) return st;
   }
   return HW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float *out, float *lse,
+                               void *stream) {
+  return decode_impl(ctx, layer, 1, q, out, lse, (hipStream_t)stream);
+}
+
+hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
+                                      float *out, float *lse, void *stream) {
+  return decode_impl(ctx, layer, n_new, q, out, lse, (hipStream_t)stream);
 }
 
 hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity) {
@@ -922,7 +966,7 @@ hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *d
   const int32_t ns = (int32_t)r.seg_blocks.size(), ng = (int32_t)r.g_page.size();
   if (n_segs) *n_segs = ns;
   if (n_groups) *n_groups = ng;
-  if (n_splits) *n_splits = choose_splits(ctx, ng, r.n_workers);
+  if (n_splits) *n_splits = choose_splits(ctx, ng, rows_total(ctx, r.n_workers));
   if (ns > cap_segs || ng > cap_groups) return ctx->fail(HW_ERR_INVALID_ARG, "buffers too small");
   if (segs) std::copy(r.seg_blocks.begin(), r.seg_blocks.end(), segs);
   if (delta) std::copy(r.delta.begin(), r.delta.end(), delta);

@@ -57,8 +57,10 @@ struct DecodeArgs {
   const float *q;          // [n_workers][n_q_heads][head_dim]
   float *out;              // [n_workers][n_q_heads][head_dim]   (written when n_splits == 1)
   float *lse;              // [n_workers][n_q_heads] or null      (idem)
-  const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens},
-                           // or wide descriptors (desc_stride = kWideStride ints per group)
+  const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens}
+                           // (desc_stride 2); with the group's first local position as a
+                           // third int (desc_stride 4, several query tokens per worker); or
+                           // wide descriptors (desc_stride = kWideStride ints per group)
   const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
   const double *turn_freq; // [head_dim/2] theta^(-2j/d) / (2 pi): rotation turns per position
   float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
@@ -72,12 +74,14 @@ struct DecodeArgs {
   int32_t n_splits;
   int32_t page_groups;
   int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)
-  float inv_group;         // 1 / group (rows < 2^22, so the worker of a row is exact in fp32)
+  float inv_group;         // 1 / group (rows < 2^22, so the query token of a row is exact in fp32)
+  float inv_rpw;           // 1 / (n_new * group): rows per worker
+  int32_t n_new;           // query tokens per worker (rows = n_workers * n_new * group)
   float q_scale;           // softmax_scale * log2(e)
   // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];
-  int32_t desc_stride;     // ints per group descriptor: 2, or kWideStride (8-wave kernels only)
+  int32_t desc_stride;     // ints per group descriptor: 2, 4, or kWideStride (8-wave kernels only)
 };
 
 
@@ -87,7 +91,7 @@ struct MergeArgs {
   const float *part_lse;
   float *out;
   float *lse;
-  int32_t n_workers;
+  int32_t n_workers;   // query tokens: workers x tokens per worker, in (worker, token) order
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t group;

@@ -313,9 +313,19 @@ constexpr float kRescaleLog2 = 8.0f;
 // Group descriptors are wave-uniform: they are read through the scalar cache (constant
 // address space), whose loads are counted apart from the vector loads of K and V.
 typedef __attribute__((address_space(4))) const int ConstInt;
-__device__ __forceinline__ int2 load_desc(const int2 *groups, long long i) {
-  const ConstInt *p = (const ConstInt *)groups;
-  return make_int2(p[2 * i], p[2 * i + 1]);
+// A group descriptor: page-group index of head 0, segment << 8 | valid tokens, and the
+// local position of the group's first token in its block (ls; read from 4-int descriptors,
+// which several-token decodes use for their causal mask; 0 otherwise).
+struct GDesc {
+  int x = 0, y = 0, ls = 0;
+};
+__device__ __forceinline__ GDesc load_desc(const int2 *groups, long long i, int stride) {
+  const ConstInt *p = (const ConstInt *)groups + (long long)stride * i;
+  GDesc d;
+  d.x = p[0];
+  d.y = p[1];
+  if (stride == 4) d.ls = p[2];
+  return d;
 }
 
 // A wide descriptor (kWideStride ints): the group's {x, y} and the query offsets of workers
@@ -326,7 +336,7 @@ static_assert(kWideWorkers == 6, "WideOff holds six offsets");
 struct WideOff {
   int o0 = -1, o1 = -1, o2 = -1, o3 = -1, o4 = -1, o5 = -1;
 };
-__device__ __forceinline__ int2 load_desc_wide(const int2 *groups, long long i, WideOff &w) {
+__device__ __forceinline__ GDesc load_desc_wide(const int2 *groups, long long i, WideOff &w) {
   const ConstInt *p = (const ConstInt *)groups + (long long)kWideStride * i;
   w.o0 = p[2];
   w.o1 = p[3];
@@ -334,7 +344,10 @@ __device__ __forceinline__ int2 load_desc_wide(const int2 *groups, long long i, 
   w.o3 = p[5];
   w.o4 = p[6];
   w.o5 = p[7];
-  return make_int2(p[0], p[1]);
+  GDesc d;
+  d.x = p[0];
+  d.y = p[1];
+  return d;
 }
 // (readfirstlane of the wave-uniform fields keeps the compiler from turning the selects
 // into one load at a computed offset, which would put the offsets in memory)
@@ -352,15 +365,16 @@ __device__ __forceinline__ int wide_pick(const WideOff &w, int k) {
 template <typename KV, int D>
 struct Stage {
   Frag<KV, D> f;
-  int desc_x, desc_y;
+  int desc_x, desc_y, desc_ls;
 };
 
 // Issue one group's K and V loads (each group is read by one wave: streaming hint).
 template <typename KV, int D>
-__device__ __forceinline__ void fetch_group(Stage<KV, D> &st, int2 desc, const KV *kl,
+__device__ __forceinline__ void fetch_group(Stage<KV, D> &st, GDesc desc, const KV *kl,
                                             const KV *vl, size_t head_groups, int lane) {
   st.desc_x = desc.x;
   st.desc_y = desc.y;
+  st.desc_ls = desc.ls;
   const size_t gb = ((size_t)desc.x + head_groups) * (size_t)(32 * D);
   st.f.template load<true>(kl + gb, vl + gb, lane);
 }
@@ -467,18 +481,28 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   const KV *vl = static_cast<const KV *>(a.v_layer);
   const size_t head_groups = (size_t)kvh * a.page_groups;
 
-  // Worker of stacked row rr = rr / group, computed as floor((rr + 0.5) * (1 / group)) in
-  // fp32: exact while rr < 2^22, as the error of the product stays below 0.5 / group.
-  auto worker_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
+  // Stacked row rr = (query token wt, head rr - wt * group of the KV head's group) with
+  // wt = rr / group, and query token wt = (worker wt / n_new, token wt % n_new): both
+  // quotients as floor((x + 0.5) * (1 / y)) in fp32, exact while rr < 2^22 (the error of
+  // the product stays below 0.5 / y). With one token per worker, wt is the worker.
+  auto tok_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
+  auto worker_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_rpw); };
+  // n_new - 1 - t for the token of row rr: it sits that many positions before q_pos
+  auto back_of = [&](int rr) { return a.n_new - 1 - (tok_of(rr) - worker_of(rr) * a.n_new); };
+  // A row's offset into a block: the worker's offset (query position minus block start,
+  // -1 if not visible) moved back to the row's token; -1 when the block starts after it.
+  auto row_offset = [](int dl, int back) { return dl < back ? -1 : dl - back; };
   // The lane's rows: row rt * 16 + col of the workgroup's block.
-  int row_w[RT];
+  int row_w[RT], row_back[RT];
   bool row_ok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + col;
     row_ok[rt] = r < nrows;
     row_w[rt] = row_ok[rt] ? worker_of(row0 + r) : 0;
+    row_back[rt] = row_ok[rt] ? back_of(row0 + r) : 0;
   }
+  const bool causal = a.n_new > 1;   // several tokens per worker: mask keys after each token
   // Workers of the block's rows: wlo .. wlo + nw - 1 (nw <= NWMAX, one per row at most).
   const int wlo = __builtin_amdgcn_readfirstlane(worker_of(row0));
   const int nw = __builtin_amdgcn_readfirstlane(worker_of(row0 + nrows - 1)) - wlo + 1;
@@ -493,16 +517,16 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // unconditionally keep the waits for each stage exact.
   int s_lo = 0, s_hi = -1;
   if (COOP && end > begin) {
-    s_lo = load_desc(a.groups, begin).y >> 8;
-    s_hi = load_desc(a.groups, end - 1).y >> 8;
+    s_lo = load_desc(a.groups, begin, a.desc_stride).y >> 8;
+    s_hi = load_desc(a.groups, end - 1, a.desc_stride).y >> 8;
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
-  int2 desc = make_int2(0, 0), next = make_int2(0, 0), next2 = make_int2(0, 0);
+  GDesc desc, next, next2;
   // WIDE: the offsets of workers 0.. for the segments of desc, next, next2
   WideOff ow, ow_next, ow_next2;
   auto desc_at = [&](long long i, WideOff &off) __attribute__((always_inline)) {
     if constexpr (WIDE) return load_desc_wide(a.groups, i, off);
-    else return load_desc(a.groups, i);
+    else return load_desc(a.groups, i, a.desc_stride);
   };
   if (wcount > 0) desc = desc_at(wfirst, ow);   // only groups of this wave's run
   if (wcount > 1) next = desc_at(wfirst + 1, ow_next);
@@ -520,8 +544,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < RT * 16 * D / 4 && r < nrows) {
       const int rr = row0 + r;
-      const int w = worker_of(rr), gq = rr - w * a.group;
-      qv[k] = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.n_q_heads + kvh * a.group + gq) * D)[d4];
+      const int wt = tok_of(rr), gq = rr - wt * a.group;
+      qv[k] = reinterpret_cast<const float4 *>(a.q + ((size_t)wt * a.n_q_heads + kvh * a.group + gq) * D)[d4];
     }
   }
   const double fq = tid < D / 2 ? a.turn_freq[tid] : 0.0;
@@ -600,7 +624,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       float lo[8], hi[8];
       bool vis = false;
       if (row < nrows) {
-        const int dl = sm_dl[sl * nw + worker_of(row0 + row) - wlo];
+        const int dl = row_offset(sm_dl[sl * nw + worker_of(row0 + row) - wlo], back_of(row0 + row));
         vis = dl >= 0;
         rotate8(qrows + row * QSTRIDE, 32 * c + 8 * (ln >> 4), vis ? dl : 0, lo, hi);
       }
@@ -614,12 +638,14 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   float m[RT], l[RT];
   bool rowvis[RT];
   bool rowmask[RT];   // wave-uniform: some real row of this tile does not see the block
+  int rowoff[RT];     // the row's offset into the current block (its keys j <= rowoff)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = -INFINITY;
     l[rt] = 0.0f;
     rowvis[rt] = false;
     rowmask[rt] = false;
+    rowoff[rt] = -1;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -638,7 +664,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         cur_seg = seg;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int dl = row_ok[rt] ? sm_dl[sl * nw + row_w[rt] - wlo] : -1;
+          const int dl = row_ok[rt] ? row_offset(sm_dl[sl * nw + row_w[rt] - wlo], row_back[rt]) : -1;
+          rowoff[rt] = dl;
           rowvis[rt] = row_ok[rt] && dl >= 0;
           rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
         }
@@ -647,14 +674,16 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        rowvis[rt] = row_ok[rt] && delta[rt] >= 0;
-        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && delta[rt] < 0) != 0;
+        const int dl = row_offset(delta[rt], row_back[rt]);
+        rowoff[rt] = dl;
+        rowvis[rt] = row_ok[rt] && dl >= 0;
+        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
       }
       if (seg != cur_seg) {
         cur_seg = seg;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int dl = delta[rt];
+          const int dl = rowoff[rt];
 #pragma unroll
           for (int c = 0; c < NC / 2; ++c) {
             float lo[8], hi[8];
@@ -696,6 +725,14 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     bool any_mask = nvalid < 32;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) any_mask |= rowmask[rt];
+    // Several tokens per worker: a visible row also loses the group's keys after its token
+    // (local position ls + u above its offset into the block).
+    const int ls = sg.desc_ls;
+    if (causal) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        any_mask |= __builtin_amdgcn_ballot_w64(rowvis[rt] && ls + nvalid - 1 > rowoff[rt]) != 0;
+    }
     if (any_mask) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -703,7 +740,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * grp + e;
           const float x = sc[rt][e >> 2][e & 3];
-          v8[rt][e] = ((rowvis[rt] || !row_ok[rt]) && u < nvalid) ? x : -INFINITY;
+          const bool key_ok = !causal || !row_ok[rt] || ls + u <= rowoff[rt];
+          v8[rt][e] = ((rowvis[rt] || !row_ok[rt]) && u < nvalid && key_ok) ? x : -INFINITY;
         }
     } else {
 #pragma unroll
@@ -767,6 +805,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       st.f.stage_read(stage, lane);
       st.desc_x = next.x;
       st.desc_y = next.y;
+      st.desc_ls = next.ls;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage read before it is refilled
       if (i + 1 < wcount) {
         const size_t gb = ((size_t)next2.x + head_groups) * (size_t)(32 * D);
@@ -818,11 +857,11 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       __syncthreads();
       while (i < wcount && (desc.y >> 8) < seg_lo + CAP) {
         st = st2;
-        fetch_group(st2, i + 1 < wcount ? next : make_int2(0, 0), kl, vl, head_groups, lane);
+        fetch_group(st2, i + 1 < wcount ? next : GDesc(), kl, vl, head_groups, lane);
         process(st, seg_lo, dl_cur);
         desc = next;
         next = next2;
-        next2 = load_desc(a.groups, min(wfirst + i + 3, wlast));
+        next2 = load_desc(a.groups, min(wfirst + i + 3, wlast), a.desc_stride);
         ++i;
       }
     }
@@ -878,10 +917,10 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     const int rr = row0 + r;
     float *dst;
     if (direct) {
-      const int w = worker_of(rr), h = kvh * a.group + rr - w * a.group;
-      dst = a.out + ((size_t)w * a.n_q_heads + h) * D;
+      const int wt = tok_of(rr), h = kvh * a.group + rr - wt * a.group;
+      dst = a.out + ((size_t)wt * a.n_q_heads + h) * D;
       if (dt == 0 && (ln >> 4) == 0 && a.lse)
-        a.lse[(size_t)w * a.n_q_heads + h] =
+        a.lse[(size_t)wt * a.n_q_heads + h] =
             L > 0.0f ? (sm_rowm[r] + __log2f(L)) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t prow = ((size_t)split * a.n_kv_heads + kvh) * a.rows + rr;

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 
 # every symbol the headers declare
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
-           "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_reset_block",
+           "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_concurrent_decode_tokens",
+           "hw_reset_block",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
            "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
            "hw_debug_stream_read", "hw_debug_partition"]
@@ -36,7 +37,8 @@ class HwConfig(ctypes.Structure):
         ("n_layers", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
         ("head_dim", c_int32), ("page_size", c_int32), ("n_pages", c_int32),
         ("max_blocks", c_int32), ("max_workers", c_int32), ("max_position", c_int32),
-        ("max_splits", c_int32), ("kv_dtype", c_int), ("page_seed", c_uint32),
+        ("max_splits", c_int32), ("max_query_tokens", c_int32), ("kv_dtype", c_int),
+        ("page_seed", c_uint32),
         ("rope_theta", c_double), ("softmax_scale", c_float),
         ("k_pool", c_void_p), ("v_pool", c_void_p),
     ]
@@ -70,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_append_kv": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_void_p, c_void_p, c_void_p]),
         "hw_set_views": (c_int, [c_void_p, c_int32, P32, P32, P64, P64]),
         "hw_concurrent_decode": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "hw_concurrent_decode_tokens": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                                c_void_p, c_void_p]),
         "hw_reset_block": (c_int, [c_void_p, c_int32]),
         "hw_set_split": (c_int, [c_void_p, c_int32]),
         "hw_block_info": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_int32, P32]),
@@ -153,6 +157,13 @@ def hw_concurrent_decode(ctx, layer: int, q_ptr: int, out_ptr: int, lse_ptr: Opt
     _check(ctx, load_library().hw_concurrent_decode(ctx, layer, c_void_p(q_ptr), c_void_p(out_ptr),
                                                     c_void_p(lse_ptr) if lse_ptr else None,
                                                     c_void_p(stream)))
+
+
+def hw_concurrent_decode_tokens(ctx, layer: int, n_new: int, q_ptr: int, out_ptr: int,
+                                lse_ptr: Optional[int], stream: int) -> None:
+    _check(ctx, load_library().hw_concurrent_decode_tokens(
+        ctx, layer, n_new, c_void_p(q_ptr), c_void_p(out_ptr),
+        c_void_p(lse_ptr) if lse_ptr else None, c_void_p(stream)))
 
 
 def hw_reset_block(ctx, block_id: int) -> None:
@@ -250,7 +261,7 @@ class HogwildCache:
                  page_size: int, n_pages: int, max_blocks: int, max_workers: int,
                  max_position: int, kv_dtype: str = "bf16", page_seed: int = 0,
                  rope_theta: float = 1e4, softmax_scale: float = 0.0, max_splits: int = 0,
-                 device: str = "cuda"):
+                 max_query_tokens: int = 0, device: str = "cuda"):
         import torch
         self.torch = torch
         load_library()
@@ -266,7 +277,7 @@ class HogwildCache:
         self.v_pool = torch.zeros(elems, dtype=self.kv_torch_dtype, device=self.device)
         self.cfg = HwConfig(n_layers, n_q_heads, n_kv_heads, head_dim, page_size, n_pages,
                             max_blocks, max_workers, max_position, max_splits,
-                            HW_BF16 if kv_dtype == "bf16" else HW_F32, page_seed,
+                            max_query_tokens, HW_BF16 if kv_dtype == "bf16" else HW_F32, page_seed,
                             rope_theta, softmax_scale, self.k_pool.data_ptr(),
                             self.v_pool.data_ptr())
         self.ctx = hw_create(self.cfg)
@@ -292,18 +303,39 @@ class HogwildCache:
         hw_set_views(self.ctx, views, offsets, q_pos)
         self.n_workers = len(views)
 
-    def decode(self, layer: int, q, out=None, lse=None, want_lse: bool = True):
-        torch = self.torch
-        shape = (self.n_workers, self.n_q_heads, self.head_dim)
-        if q.dtype != torch.float32 or tuple(q.shape) != shape or not q.is_contiguous() \
-                or q.device != self.device:
-            raise HwError(HW_ERR_INVALID_ARG, f"q must be contiguous float32 {shape} on {self.device}")
+    def _f32(self, name: str, t, shape) -> None:
+        if t.dtype != self.torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+                or t.device != self.device:
+            raise HwError(HW_ERR_INVALID_ARG, f"{name} must be contiguous float32 {tuple(shape)} "
+                                              f"on {self.device}")
+
+    def _io(self, q, out, lse, want_lse, shape):
+        self._f32("q", q, shape)
         if out is None:
-            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+            out = self.torch.empty(shape, dtype=self.torch.float32, device=self.device)
+        self._f32("out", out, shape)
         if lse is None and want_lse:
-            lse = torch.empty(shape[:2], dtype=torch.float32, device=self.device)
+            lse = self.torch.empty(shape[:-1], dtype=self.torch.float32, device=self.device)
+        if lse is not None:
+            self._f32("lse", lse, shape[:-1])
+        return out, lse
+
+    def decode(self, layer: int, q, out=None, lse=None, want_lse: bool = True):
+        """One query token per worker: q [n_workers, n_q_heads, head_dim] float32."""
+        out, lse = self._io(q, out, lse, want_lse, (self.n_workers, self.n_q_heads, self.head_dim))
         hw_concurrent_decode(self.ctx, layer, q.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None, self._stream())
+        return out, lse
+
+    def decode_tokens(self, layer: int, q, out=None, lse=None, want_lse: bool = True):
+        """n_new query tokens per worker, causal: q [n_workers, n_new, n_q_heads, head_dim]."""
+        if q.dim() != 4:
+            raise HwError(HW_ERR_INVALID_ARG, "q must be [n_workers, n_new, n_q_heads, head_dim]")
+        n_new = int(q.shape[1])
+        out, lse = self._io(q, out, lse, want_lse,
+                            (self.n_workers, n_new, self.n_q_heads, self.head_dim))
+        hw_concurrent_decode_tokens(self.ctx, layer, n_new, q.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, self._stream())
         return out, lse
 
     def block_info(self, block: int, layer: int = 0):

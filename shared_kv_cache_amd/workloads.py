@@ -23,6 +23,7 @@ import numpy as np
 _STRUCTURE = 0xFFFF_FFFF  # tensor id reserved for structural draws
 _Q_ID = 0
 _STEP_BASE = 1 << 24      # tensor ids of per-step appended tokens
+_TOKENS_BASE = 1 << 23    # tensor ids of several-token queries
 
 
 def _rng(*words: int) -> np.random.Generator:
@@ -139,6 +140,12 @@ class Workload:
         """Raw queries [N, Hq, D] fp32 (the query dtype is always fp32)."""
         tid = _Q_ID if step == 0 else _STEP_BASE + 2 * step + 1
         return self._draw(layer, tid, (self.n_workers, self.n_q_heads, self.head_dim))
+
+    def q_tokens(self, layer: int, n_new: int) -> np.ndarray:
+        """Raw queries of n_new tokens per worker [N, n_new, Hq, D] fp32 (the tokens a worker
+        appends together, e.g. a paragraph header opening a fresh block)."""
+        return self._draw(layer, _TOKENS_BASE + n_new,
+                          (self.n_workers, n_new, self.n_q_heads, self.head_dim))
 
     def step_kv(self, layer: int, step: int):
         """The one new token each worker appends at decode step ``step`` >= 1:

@@ -18,7 +18,8 @@ def kv_tensor(x: np.ndarray, kv_dtype: str) -> torch.Tensor:
 
 
 def make_cache(wl: W.Workload, n_layers=None, page_seed=None, max_splits=0, n_pages=None,
-               max_blocks=None, max_position=None, max_workers=None) -> H.HogwildCache:
+               max_blocks=None, max_position=None, max_workers=None,
+               max_query_tokens=0) -> H.HogwildCache:
     return H.HogwildCache(
         n_layers=wl.n_layers if n_layers is None else n_layers,
         n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
@@ -27,7 +28,7 @@ def make_cache(wl: W.Workload, n_layers=None, page_seed=None, max_splits=0, n_pa
         max_workers=wl.n_workers if max_workers is None else max_workers,
         max_position=wl.max_position if max_position is None else max_position,
         kv_dtype=wl.kv_dtype, page_seed=wl.page_seed if page_seed is None else page_seed,
-        rope_theta=wl.theta, max_splits=max_splits)
+        rope_theta=wl.theta, max_splits=max_splits, max_query_tokens=max_query_tokens)
 
 
 def fill_layer(cache: H.HogwildCache, wl: W.Workload, layer: int, blocks=None):
@@ -64,6 +65,35 @@ def decode_np(cache: H.HogwildCache, layer: int, q: np.ndarray):
     out, lse = cache.decode(layer, qt)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def decode_tokens_np(cache: H.HogwildCache, layer: int, q: np.ndarray):
+    """Several query tokens per worker: q [N, n_new, Hq, D]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(DEV)
+    out, lse = cache.decode_tokens(layer, qt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+VARIANT_LENGTHS = [33, 1, 64, 65, 7, 0, 31, 32]
+
+
+def variant_workload(head_dim, n_workers, group):
+    """bf16 workload with n_workers * group rows per KV head: a ragged 300-token history and
+    ragged in-progress blocks (one of them empty), 32-token pages."""
+    base = W.make("tiny_fp32")
+    inprog = list(range(1, n_workers + 1))
+    lengths = {0: 300}
+    lengths.update({b: VARIANT_LENGTHS[(b - 1) % len(VARIANT_LENGTHS)] for b in inprog})
+    owners = {0: -1}
+    owners.update({b: b - 1 for b in inprog})
+    pages = sum(-(-n // 32) for n in lengths.values()) + 4
+    return W.Workload(**{**base.__dict__, "name": f"d{head_dim}_rows{n_workers * group}",
+                         "n_workers": n_workers, "n_q_heads": 2 * group, "n_kv_heads": 2,
+                         "head_dim": head_dim, "kv_dtype": "bf16", "value_scale": 1.0,
+                         "inprogress": inprog, "lengths": lengths, "owners": owners,
+                         "n_pages": pages,
+                         "max_position": max(2048, -(-(sum(lengths.values()) + 1) // 1024) * 1024)})
 
 
 def k_pool_token(cache: H.HogwildCache, layer: int, page: int, head: int, slot: int):

@@ -16,7 +16,7 @@ from shared_kv_cache_amd import hogwild as H
 from shared_kv_cache_amd import workloads as W
 
 from hw_testlib import (DEV, decode_np, fill_layer, k_pool_token, kv_tensor, make_cache, max_row_rel,
-                        oracle_blocks, rel_l2, v_pool_token)
+                        oracle_blocks, rel_l2, v_pool_token, variant_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -184,27 +184,6 @@ def test_many_rows_multiple_row_blocks_and_empty_view():
     cache.close()
 
 
-_VARIANT_LENGTHS = [33, 1, 64, 65, 7, 0, 31, 32]
-
-
-def _variant_workload(head_dim, n_workers, group):
-    """bf16 workload with n_workers * group rows per KV head: a ragged 300-token history and
-    ragged in-progress blocks (one of them empty), 32-token pages."""
-    base = W.make("tiny_fp32")
-    inprog = list(range(1, n_workers + 1))
-    lengths = {0: 300}
-    lengths.update({b: _VARIANT_LENGTHS[(b - 1) % len(_VARIANT_LENGTHS)] for b in inprog})
-    owners = {0: -1}
-    owners.update({b: b - 1 for b in inprog})
-    pages = sum(-(-n // 32) for n in lengths.values()) + 4
-    return W.Workload(**{**base.__dict__, "name": f"d{head_dim}_rows{n_workers * group}",
-                         "n_workers": n_workers, "n_q_heads": 2 * group, "n_kv_heads": 2,
-                         "head_dim": head_dim, "kv_dtype": "bf16", "value_scale": 1.0,
-                         "inprogress": inprog, "lengths": lengths, "owners": owners,
-                         "n_pages": pages,
-                         "max_position": max(2048, -(-(sum(lengths.values()) + 1) // 1024) * 1024)})
-
-
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("n_workers,group", [(2, 8), (4, 8), (5, 8), (8, 8), (3, 5), (6, 8),
                                              (7, 6), (16, 2), (9, 7), (32, 2), (64, 1), (13, 5)])
@@ -216,7 +195,7 @@ def test_every_bf16_kernel_variant(head_dim, n_workers, group):
     # take the per-row rotation, and 13 workers of 5 heads mix both in one launch.
     # Partition counts: automatic, 1, 3, 40 and 80 (bounds chosen by the host; many
     # partitions empty at 80).
-    wl = _variant_workload(head_dim, n_workers, group)
+    wl = variant_workload(head_dim, n_workers, group)
     cache = make_cache(wl, max_blocks=n_workers + 2, max_splits=128)
     fill_layer(cache, wl, 0)
     cache.set_views(wl.views())

@@ -24,7 +24,7 @@ FAKE_K, FAKE_V = 1 << 20, 2 << 20       # never dereferenced by host-only calls
 def make_cfg(**kw):
     base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=64, n_pages=16,
                 max_blocks=16, max_workers=4, max_position=4096, max_splits=0,
-                kv_dtype=H.HW_BF16, page_seed=0, rope_theta=1e4, softmax_scale=0.0,
+                max_query_tokens=0, kv_dtype=H.HW_BF16, page_seed=0, rope_theta=1e4, softmax_scale=0.0,
                 k_pool=FAKE_K, v_pool=FAKE_V)
     base.update(kw)
     return H.HwConfig(**base)
@@ -55,13 +55,23 @@ def test_library_exports_every_declared_symbol():
 @pytest.mark.parametrize("field,value", [
     ("n_layers", 0), ("n_q_heads", 7), ("n_kv_heads", 0), ("head_dim", 96), ("page_size", 48),
     ("n_pages", 0), ("max_blocks", 0), ("max_workers", 0), ("max_position", 0),
-    ("max_splits", -1), ("kv_dtype", 7), ("rope_theta", 1.0), ("softmax_scale", -1.0),
+    ("max_splits", -1), ("max_query_tokens", -1), ("max_query_tokens", 1025),
+    ("kv_dtype", 7), ("rope_theta", 1.0), ("softmax_scale", -1.0),
     ("k_pool", 0), ("v_pool", FAKE_V + 8),
 ])
 def test_create_rejects_bad_config(field, value):
     with pytest.raises(H.HwError) as e:
         H.hw_create(make_cfg(**{field: value}))
     assert e.value.status == H.HW_ERR_INVALID_ARG and e.value.message
+
+
+def test_create_bounds_stacked_rows():
+    # (worker, query token, head) rows of one KV head must stay below 2^22 (the kernels'
+    # fp32 row -> (token, worker) division is exact there)
+    H.hw_destroy(H.hw_create(make_cfg(max_workers=1024, max_query_tokens=1023, n_q_heads=8)))
+    with pytest.raises(H.HwError) as e:
+        H.hw_create(make_cfg(max_workers=1024, max_query_tokens=1024, n_q_heads=8))
+    assert e.value.status == H.HW_ERR_INVALID_ARG
 
 
 def test_workspace_size_formula(ctx):
@@ -74,6 +84,13 @@ def test_workspace_size_formula(ctx):
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
     assert H.hw_workspace_bytes(ctx) == expect
+    # several query tokens per worker: partials for every (worker, token, head) row
+    c3 = H.hw_create(make_cfg(max_query_tokens=3))
+    rows3 = 4 * 3 * 4
+    expect3 = expect - al(256 * 2 * rows * d * 4) - al(256 * 2 * rows * 4)
+    expect3 += al(256 * 2 * rows3 * d * 4) + al(256 * 2 * rows3 * 4)
+    assert H.hw_workspace_bytes(c3) == expect3
+    H.hw_destroy(c3)
 
 
 def test_calls_without_workspace_or_views(ctx):
@@ -83,6 +100,13 @@ def test_calls_without_workspace_or_views(ctx):
     with pytest.raises(H.HwError) as e:
         H.hw_concurrent_decode(ctx, 0, FAKE_K, FAKE_V, None, 0)
     assert e.value.status == H.HW_ERR_WORKSPACE
+    with pytest.raises(H.HwError) as e:
+        H.hw_concurrent_decode_tokens(ctx, 0, 1, FAKE_K, FAKE_V, None, 0)
+    assert e.value.status == H.HW_ERR_WORKSPACE
+    for n_new in (0, 2):          # max_query_tokens is 1 here
+        with pytest.raises(H.HwError) as e:
+            H.hw_concurrent_decode_tokens(ctx, 0, n_new, FAKE_K, FAKE_V, None, 0)
+        assert e.value.status == H.HW_ERR_INVALID_ARG
     with pytest.raises(H.HwError) as e:
         H.hw_debug_resolve(ctx, 0, 1)
     assert e.value.status == H.HW_ERR_STALE_VIEW
