@@ -319,12 +319,13 @@ typedef __attribute__((address_space(4))) const int ConstInt;
 struct GDesc {
   int x = 0, y = 0, ls = 0;
 };
+template <bool MT>
 __device__ __forceinline__ GDesc load_desc(const int2 *groups, long long i, int stride) {
   const ConstInt *p = (const ConstInt *)groups + (long long)stride * i;
   GDesc d;
   d.x = p[0];
   d.y = p[1];
-  if (stride == 4) d.ls = p[2];
+  if constexpr (MT) d.ls = p[2];
   return d;
 }
 
@@ -422,10 +423,14 @@ constexpr int phase_segments() {
 // WIDE wave then also keeps its next group in flight while it computes one: the next group
 // streams straight into a per-wave LDS stage (LDS-DMA loads) and moves to registers once the
 // group is done; the rotated query operands stay in registers.
-template <typename KV, int D, int RT, int NW, int NST, bool WIDE>
+//
+// MT (several query tokens per worker, 4-int descriptors): rows are (worker, token, head) and
+// each row's keys after its token are masked. One-token kernels carry none of that state.
+template <typename KV, int D, int RT, int NW, int NST, bool WIDE, bool MT>
 __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
   static_assert(NST == 1 || NST == 2, "one or two stages");
   static_assert(!WIDE || NST == 1, "wide descriptors: single-stage kernels");
+  static_assert(!(WIDE && MT), "wide descriptors: one token per worker");
   constexpr bool COOP = NST == 2;
   using F = Frag<KV, D>;
   using S = Stage<KV, D>;
@@ -486,12 +491,21 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // quotients as floor((x + 0.5) * (1 / y)) in fp32, exact while rr < 2^22 (the error of
   // the product stays below 0.5 / y). With one token per worker, wt is the worker.
   auto tok_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
-  auto worker_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_rpw); };
+  auto worker_of = [&](int rr) {
+    if constexpr (MT) return (int)(((float)rr + 0.5f) * a.inv_rpw);
+    else return tok_of(rr);
+  };
   // n_new - 1 - t for the token of row rr: it sits that many positions before q_pos
-  auto back_of = [&](int rr) { return a.n_new - 1 - (tok_of(rr) - worker_of(rr) * a.n_new); };
+  auto back_of = [&](int rr) {
+    if constexpr (MT) return a.n_new - 1 - (tok_of(rr) - worker_of(rr) * a.n_new);
+    else return 0;
+  };
   // A row's offset into a block: the worker's offset (query position minus block start,
   // -1 if not visible) moved back to the row's token; -1 when the block starts after it.
-  auto row_offset = [](int dl, int back) { return dl < back ? -1 : dl - back; };
+  auto row_offset = [](int dl, int back) {
+    if constexpr (MT) return dl < back ? -1 : dl - back;
+    else return dl;
+  };
   // The lane's rows: row rt * 16 + col of the workgroup's block.
   int row_w[RT], row_back[RT];
   bool row_ok[RT];
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     row_w[rt] = row_ok[rt] ? worker_of(row0 + r) : 0;
     row_back[rt] = row_ok[rt] ? back_of(row0 + r) : 0;
   }
-  const bool causal = a.n_new > 1;   // several tokens per worker: mask keys after each token
+  constexpr bool causal = MT;   // several tokens per worker: mask keys after each token
   // Workers of the block's rows: wlo .. wlo + nw - 1 (nw <= NWMAX, one per row at most).
   const int wlo = __builtin_amdgcn_readfirstlane(worker_of(row0));
   const int nw = __builtin_amdgcn_readfirstlane(worker_of(row0 + nrows - 1)) - wlo + 1;
@@ -517,8 +531,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // unconditionally keep the waits for each stage exact.
   int s_lo = 0, s_hi = -1;
   if (COOP && end > begin) {
-    s_lo = load_desc(a.groups, begin, a.desc_stride).y >> 8;
-    s_hi = load_desc(a.groups, end - 1, a.desc_stride).y >> 8;
+    s_lo = load_desc<MT>(a.groups, begin, a.desc_stride).y >> 8;
+    s_hi = load_desc<MT>(a.groups, end - 1, a.desc_stride).y >> 8;
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   GDesc desc, next, next2;
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   WideOff ow, ow_next, ow_next2;
   auto desc_at = [&](long long i, WideOff &off) __attribute__((always_inline)) {
     if constexpr (WIDE) return load_desc_wide(a.groups, i, off);
-    else return load_desc(a.groups, i, a.desc_stride);
+    else return load_desc<MT>(a.groups, i, a.desc_stride);
   };
   if (wcount > 0) desc = desc_at(wfirst, ow);   // only groups of this wave's run
   if (wcount > 1) next = desc_at(wfirst + 1, ow_next);
@@ -728,7 +742,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // Several tokens per worker: a visible row also loses the group's keys after its token
     // (local position ls + u above its offset into the block).
     const int ls = sg.desc_ls;
-    if (causal) {
+    if constexpr (causal) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         any_mask |= __builtin_amdgcn_ballot_w64(rowvis[rt] && ls + nvalid - 1 > rowoff[rt]) != 0;
@@ -861,7 +875,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         process(st, seg_lo, dl_cur);
         desc = next;
         next = next2;
-        next2 = load_desc(a.groups, min(wfirst + i + 3, wlast), a.desc_stride);
+        next2 = load_desc<MT>(a.groups, min(wfirst + i + 3, wlast), a.desc_stride);
         ++i;
       }
     }
@@ -1025,38 +1039,46 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 // Launched with hipExtLaunchKernelGGL so that optional start/stop events are recorded by
 // the kernel's own dispatch (null events: a plain launch). bf16 pools: up to 32 rows per
 // workgroup run on 8 single-stage waves; 33..64 rows on 4 two-stage waves.
-template <int D>
+template <int D, bool MT>
 static void launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
                                hipEvent_t e1) {
   const dim3 b8(8 * 64), b4(4 * 64);
-  const bool wide = a.desc_stride == kWideStride;
-  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, true>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, true>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false>), grid, b4, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false>), grid, b4, 0, s, e0, e1, 0, a);
+  const bool wide = !MT && a.desc_stride == kWideStride;
+  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
 }
 
+template <int D, bool MT>
+static void launch_decode_f32(const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 b8(8 * 64);
+  if (!MT && a.desc_stride == kWideStride)
+    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else
+    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+}
+
+// Several query tokens per worker (n_new > 1) run the MT kernels; wide descriptors are only
+// uploaded for one token.
 hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row_blocks,
                          hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int rows_first = a.rows < a.rows_per_block ? a.rows : a.rows_per_block;
   const int rt = (rows_first + 15) / 16;
   dim3 grid(a.n_splits, a.n_kv_heads, row_blocks);
-  dim3 block(8 * 64);
+  const bool mt = a.n_new > 1;
   if (dt == HW_BF16) {
-    if (head_dim == 128) launch_decode_bf16<128>(rt, a, grid, s, ev_start, ev_stop);
-    else launch_decode_bf16<64>(rt, a, grid, s, ev_start, ev_stop);
+    if (head_dim == 128) mt ? launch_decode_bf16<128, true>(rt, a, grid, s, ev_start, ev_stop)
+                            : launch_decode_bf16<128, false>(rt, a, grid, s, ev_start, ev_stop);
+    else mt ? launch_decode_bf16<64, true>(rt, a, grid, s, ev_start, ev_stop)
+            : launch_decode_bf16<64, false>(rt, a, grid, s, ev_start, ev_stop);
   } else {   // fp32 pools: one 16-row tile per workgroup
-    const bool wide = a.desc_stride == kWideStride;
-    if (head_dim == 128 && wide)
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1, true>), grid, block, 0, s, ev_start, ev_stop, 0, a);
-    else if (head_dim == 128)
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 128, 1, 8, 1, false>), grid, block, 0, s, ev_start, ev_stop, 0, a);
-    else if (wide)
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1, true>), grid, block, 0, s, ev_start, ev_stop, 0, a);
-    else
-      hipExtLaunchKernelGGL((concurrent_decode_kernel<float, 64, 1, 8, 1, false>), grid, block, 0, s, ev_start, ev_stop, 0, a);
+    if (head_dim == 128) mt ? launch_decode_f32<128, true>(a, grid, s, ev_start, ev_stop)
+                            : launch_decode_f32<128, false>(a, grid, s, ev_start, ev_stop);
+    else mt ? launch_decode_f32<64, true>(a, grid, s, ev_start, ev_stop)
+            : launch_decode_f32<64, false>(a, grid, s, ev_start, ev_stop);
   }
   return hipGetLastError();
 }
