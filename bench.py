@@ -75,6 +75,9 @@ def main() -> int:
     ap.add_argument("--layout", default="combined",
                     choices=["combined", "stepwise", "contiguous", "nosync"],
                     help="cache layout the views follow (combined: the method's own)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the whole step captured as one HIP graph (workloads "
+                         "whose views do not change between steps)")
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="query tokens per worker and step (several: one causal decode of all)")
     args = ap.parse_args()
@@ -175,6 +178,28 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        if grows:
+            print("--graph needs a workload whose views stay the same between steps", file=sys.stderr)
+            return 2
+        # The tables of the views are uploaded by the warm-up steps; the captured step holds
+        # only the decode and merge launches of every layer.
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            stream = side.cuda_stream
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            step()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
 
     # Timed region 1: headline wall clock, no instrumentation.
     t_tok0 = tokens_now()
@@ -182,7 +207,10 @@ def main() -> int:
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     ev1.record()
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
@@ -234,7 +262,7 @@ def main() -> int:
             "step_ideal_bytes": int(step_bytes), "step_GBps": round(step_gbps, 1),
             "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
             "decode_kernel_us": round(dec_avg * 1e3, 3),
-            "appends_per_step": L if grows else 0, "query_tokens": kq,
+            "appends_per_step": L if grows else 0, "query_tokens": kq, "hip_graph": graph is not None,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
