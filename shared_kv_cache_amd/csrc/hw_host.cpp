@@ -304,6 +304,13 @@ void partition_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, 
     for (int32_t q = 0; q <= n; ++q) out[q] = 0;
     return;
   }
+  if (alpha == 0.0) {
+    // One unit per group: the even split (floor or ceil of G / n groups each) is optimal, and
+    // unlike packing at the bound it leaves no short partitions at the end, so the bytes each
+    // XCD streams come out even.
+    for (int32_t q = 0; q <= n; ++q) out[q] = (int32_t)((int64_t)G * q / n);
+    return;
+  }
   int64_t starts = 0;
   for (int32_t i = 0; i < G; ++i) starts += (first[i] || i == 0) ? 1 : 0;
   double lo = std::max(1.0 + alpha, ((double)G + alpha * (double)starts) / (double)n);
@@ -323,10 +330,13 @@ void partition_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, 
 #ifndef HW_SPLIT_ALPHA_COOP
 #define HW_SPLIT_ALPHA_COOP 2.0
 #endif
+#ifndef HW_SPLIT_ALPHA_8W
+#define HW_SPLIT_ALPHA_8W 0.0
+#endif
 double split_alpha(const hw_ctx *c, int32_t rows) {
   const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
   const int32_t first = std::min(rows, rpb);
-  return (c->cfg.kv_dtype == HW_BF16 && first > 32) ? HW_SPLIT_ALPHA_COOP : 0.0;
+  return (c->cfg.kv_dtype == HW_BF16 && first > 32) ? HW_SPLIT_ALPHA_COOP : HW_SPLIT_ALPHA_8W;
 }
 
 int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {

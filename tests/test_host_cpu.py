@@ -433,11 +433,11 @@ def test_partition_bounds_are_min_max_optimal():
 
 
 def test_partition_without_block_weight_is_balanced():
-    # alpha 0: partitions of ceil(G / n) groups (the last one takes the remainder)
-    for g, n in [(1149, 24), (541, 24), (7, 3), (5, 8), (256, 256)]:
+    # alpha 0: partitions of floor(G / n) or ceil(G / n) groups (the even split)
+    for g, n in [(1149, 24), (541, 24), (560, 24), (7, 3), (5, 8), (256, 256), (1000, 7)]:
         b = H.hw_debug_partition([1] + [0] * (g - 1), n, 0.0)
         sizes = [b[i + 1] - b[i] for i in range(n)]
-        assert max(sizes) == -(-g // n) and sum(sizes) == g
+        assert max(sizes) == -(-g // n) and min(sizes) == g // n and sum(sizes) == g, sizes
 
 
 def test_partition_gives_block_rich_ranges_fewer_groups():
