@@ -466,7 +466,10 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   const int lane = tid & 63;
   const int wave = wave_slot();
   const int col = lane & 15, grp = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y;
+  // Grid (KV head, partition, row block): dispatch deals consecutive workgroups to the 8 XCDs
+  // in turn, so with 8 KV heads each XCD takes one head's partitions, the same mix of the
+  // group list on every XCD.
+  const int kvh = blockIdx.x, split = blockIdx.y;
   const int row0 = blockIdx.z * a.rows_per_block;
   const int nrows = min(a.rows_per_block, a.rows - row0);
   QOp *qt = reinterpret_cast<QOp *>(smem + (LDSST ? 0 : Q_FLOATS));
@@ -1067,7 +1070,7 @@ hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row
                          hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int rows_first = a.rows < a.rows_per_block ? a.rows : a.rows_per_block;
   const int rt = (rows_first + 15) / 16;
-  dim3 grid(a.n_splits, a.n_kv_heads, row_blocks);
+  dim3 grid(a.n_kv_heads, a.n_splits, row_blocks);
   const bool mt = a.n_new > 1;
   if (dt == HW_BF16) {
     if (head_dim == 128) mt ? launch_decode_bf16<128, true>(rt, a, grid, s, ev_start, ev_stop)
