@@ -269,8 +269,8 @@ void commit_append(hw_ctx *c, int32_t layer, int32_t n_blocks, const int32_t *id
 
 // ---- view resolution ---------------------------------------------------------------
 
-int32_t row_blocks_for(const hw_ctx *c, int32_t rows) {
-  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
+int32_t row_blocks_for(const hw_ctx *c, int32_t rows, int32_t n_new = 1) {
+  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype, n_new);
   return std::max(1, (rows + rpb - 1) / rpb);
 }
 
@@ -333,14 +333,14 @@ void partition_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, 
 #ifndef HW_SPLIT_ALPHA_8W
 #define HW_SPLIT_ALPHA_8W 0.0
 #endif
-double split_alpha(const hw_ctx *c, int32_t rows) {
-  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype);
+double split_alpha(const hw_ctx *c, int32_t rows, int32_t n_new = 1) {
+  const int32_t rpb = hw::rows_per_block(c->cfg.kv_dtype, n_new);
   const int32_t first = std::min(rows, rpb);
   return (c->cfg.kv_dtype == HW_BF16 && first > 32) ? HW_SPLIT_ALPHA_COOP : HW_SPLIT_ALPHA_8W;
 }
 
-int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {
-  const int32_t row_blocks = row_blocks_for(c, rows);
+int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows, int32_t n_new = 1) {
+  const int32_t row_blocks = row_blocks_for(c, rows, n_new);
   const int32_t per_head = c->cfg.n_kv_heads * std::max(1, row_blocks);
   // Workgroups for about three quarters of the CUs: measured on MI355X, this still keeps
   // HBM saturated while each wave takes more groups (fixed per-wave costs amortised, less
@@ -350,9 +350,9 @@ int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {
   return std::max(1, std::min(s, c->cfg.max_splits));
 }
 
-int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t rows) {
+int32_t choose_splits(const hw_ctx *c, int32_t n_groups, int32_t rows, int32_t n_new = 1) {
   return c->split_override > 0 ? std::min(c->split_override, c->cfg.max_splits)
-                               : auto_splits(c, n_groups, rows);
+                               : auto_splits(c, n_groups, rows, n_new);
 }
 
 // Signature of everything a resolution depends on; equal signatures => equal tables.
@@ -751,7 +751,7 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
     return ctx->fail(HW_ERR_STALE_VIEW, "a worker's first query token would sit below position 0");
 
   const int32_t n_groups = ctx->up_n_groups;
-  const int32_t splits = choose_splits(ctx, n_groups, rows);
+  const int32_t splits = choose_splits(ctx, n_groups, rows, n_new);
   const size_t eb = kv_elem_bytes(ctx);
   hw::DecodeArgs a{};
   a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
@@ -772,14 +772,14 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
   a.rows = rows;
   a.n_splits = splits;
   a.page_groups = g.page_size / hw::kTokGroup;
-  a.rows_per_block = hw::rows_per_block(g.kv_dtype);
+  a.rows_per_block = hw::rows_per_block(g.kv_dtype, n_new);
   a.inv_group = 1.0f / (float)group;
   a.inv_rpw = 1.0f / (float)(n_new * group);
   a.n_new = n_new;
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
   a.desc_stride = ctx->up_stride;
   if (splits <= hw::kMaxBoundSplits) {
-    const double alpha = split_alpha(ctx, rows);
+    const double alpha = split_alpha(ctx, rows, n_new);
     if (ctx->bounds_splits != splits || ctx->bounds_alpha != alpha) {
       ctx->bounds.resize((size_t)splits + 1);
       partition_bounds(ctx->up_seg_first.data(), n_groups, splits, alpha, ctx->bounds.data());
@@ -788,7 +788,7 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
     }
     std::copy(ctx->bounds.begin(), ctx->bounds.end(), a.split_begin);
   }
-  const int32_t row_blocks = row_blocks_for(ctx, rows);
+  const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
   hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
   hw_status st = post_launch(ctx,

@@ -1043,16 +1043,18 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 // the kernel's own dispatch (null events: a plain launch). bf16 pools: up to 32 rows per
 // workgroup run on 8 single-stage waves; 33..64 rows on 4 two-stage waves.
 template <int D, bool MT>
-static void launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0,
-                               hipEvent_t e1) {
+static hipError_t launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hipStream_t s,
+                                     hipEvent_t e0, hipEvent_t e1) {
   const dim3 b8(8 * 64), b4(4 * 64);
   const bool wide = !MT && a.desc_stride == kWideStride;
   if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if constexpr (MT) return hipErrorInvalidValue;   // several tokens: blocks of <= 32 rows
   else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
   else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
+  return hipSuccess;
 }
 
 template <int D, bool MT>
@@ -1073,10 +1075,12 @@ hipError_t launch_decode(hw_dtype dt, int head_dim, const DecodeArgs &a, int row
   dim3 grid(a.n_kv_heads, a.n_splits, row_blocks);
   const bool mt = a.n_new > 1;
   if (dt == HW_BF16) {
-    if (head_dim == 128) mt ? launch_decode_bf16<128, true>(rt, a, grid, s, ev_start, ev_stop)
-                            : launch_decode_bf16<128, false>(rt, a, grid, s, ev_start, ev_stop);
-    else mt ? launch_decode_bf16<64, true>(rt, a, grid, s, ev_start, ev_stop)
-            : launch_decode_bf16<64, false>(rt, a, grid, s, ev_start, ev_stop);
+    const hipError_t e = head_dim == 128
+                             ? (mt ? launch_decode_bf16<128, true>(rt, a, grid, s, ev_start, ev_stop)
+                                   : launch_decode_bf16<128, false>(rt, a, grid, s, ev_start, ev_stop))
+                             : (mt ? launch_decode_bf16<64, true>(rt, a, grid, s, ev_start, ev_stop)
+                                   : launch_decode_bf16<64, false>(rt, a, grid, s, ev_start, ev_stop));
+    if (e != hipSuccess) return e;
   } else {   // fp32 pools: one 16-row tile per workgroup
     if (head_dim == 128) mt ? launch_decode_f32<128, true>(a, grid, s, ev_start, ev_stop)
                             : launch_decode_f32<128, false>(a, grid, s, ev_start, ev_stop);

@@ -4,8 +4,8 @@ fp64 oracle's causal several-token attention, through the C ABI.
 Token t of worker w sits at q_pos(w) - (n_new - 1 - t) and sees only the keys of w's view
 at or before it (paper summary s8 step 4: a worker that opens a fresh block appends its
 paragraph header, and the header's tokens are attended together). Rows of a KV head are
-(worker, token, head), so these shapes reach every decode kernel: the 8-wave kernels with
-narrow descriptors, the 4-wave cooperative kernels, several row blocks, fp32 pools.
+(worker, token, head), in blocks of at most 32 rows (bf16) or 16 (fp32) on the 8-wave
+kernels: these shapes take one to six row blocks, one and two row tiles, both head sizes.
 Tolerances as for one token: relative L2 <= 1e-2 (bf16 K/V), <= 1e-5 (fp32).
 """
 
@@ -41,13 +41,13 @@ def _compare(name, out, lse, ref, ref_lse, tol):
 
 
 @pytest.mark.parametrize("head_dim,n_workers,group,n_new,kv_dtype", [
-    (128, 2, 8, 2, "bf16"),    # 32 rows: 8-wave kernel, two row tiles, 4-int descriptors
-    (64, 4, 8, 2, "bf16"),     # 64 rows: 4-wave cooperative kernel
-    (64, 3, 5, 5, "bf16"),     # 75 rows: two row blocks; a token's heads straddle tiles
-    (128, 16, 2, 3, "bf16"),   # 96 rows of 16 workers
-    (64, 1, 1, 7, "bf16"),     # one worker, one head per KV head: 7 rows
-    (128, 6, 8, 4, "bf16"),    # 192 rows: three row blocks
-    (128, 3, 2, 3, "f32"),     # fp32 pools: 16-row blocks
+    (128, 2, 8, 2, "bf16"),    # 32 rows: one block of two row tiles, 4-int descriptors
+    (64, 4, 8, 2, "bf16"),     # 64 rows: two blocks
+    (64, 3, 5, 5, "bf16"),     # 75 rows: blocks of 32, 32, 11; a token's heads straddle blocks
+    (128, 16, 2, 3, "bf16"),   # 96 rows of 16 workers: three blocks
+    (64, 1, 1, 7, "bf16"),     # one worker, one head per KV head: 7 rows, one tile
+    (128, 6, 8, 4, "bf16"),    # 192 rows: six blocks
+    (128, 3, 2, 3, "f32"),     # fp32 pools: 18 rows in blocks of 16 and 2
 ])
 def test_several_query_tokens_per_worker(head_dim, n_workers, group, n_new, kv_dtype):
     # The variant workload's own blocks hold 33, 1, 64, 65, 7, 0, 31, 32 tokens: a worker
