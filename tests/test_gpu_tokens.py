@@ -191,3 +191,70 @@ def test_w4_16k_header_tokens_sampled_heads():
     _compare("w4_16k 4 tokens", out[:, :, heads], lse[:, :, heads], ref[:, :, heads],
              ref_lse[:, :, heads], TOL["bf16"])
     cache.close()
+
+
+def test_w8_32k_header_tokens_sampled_heads():
+    # The w8_32k cache (32k-token common history in scattered 256-token pages, 64 query heads
+    # over 8 KV heads, 8 workers): four tokens per worker make 256 rows per KV head, eight
+    # row blocks, in the launch configuration the bench times.
+    wl = W.make("w8_32k", n_layers=1)
+    cache = make_cache(wl, max_query_tokens=4)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    q = wl.q_tokens(0, 4)
+    out, lse = decode_tokens_np(cache, 0, q)
+    # the oracle on sampled workers (first, middle, last) and heads: each worker's result
+    # depends only on its own view
+    rng = np.random.default_rng(wl.seed + 8)
+    heads = sorted(int(x) for x in rng.choice(wl.n_q_heads, size=4, replace=False))
+    sel = [0, 3, 7]
+    views = wl.views()
+    ref, ref_lse = O.concurrent_attention(q[sel].astype(np.float64), oracle_blocks(wl, 0),
+                                          [views[w] for w in sel], theta=wl.theta, heads=heads)
+    _compare("w8_32k 4 tokens", out[sel][:, :, heads], lse[sel][:, :, heads], ref[:, :, heads],
+             ref_lse[:, :, heads], TOL["bf16"])
+    cache.close()
+
+
+def test_several_tokens_graph_replays_equal_eager():
+    # A two-layer several-token decode captured as one HIP graph (after the tables are
+    # uploaded): every replay, with eager work in between, equals the eager result bit for bit.
+    wl = variant_workload(128, 4, 8)
+    wl = W.Workload(**{**wl.__dict__, "n_layers": 2})
+    cache = make_cache(wl, max_blocks=8, max_query_tokens=3)
+    for layer in range(2):
+        fill_layer(cache, wl, layer)
+    cache.set_views(wl.views())
+    qs = [torch.from_numpy(wl.q_tokens(layer, 3)).to(DEV) for layer in range(2)]
+    outs = [torch.empty_like(q) for q in qs]
+    lses = [torch.empty(q.shape[:3], device=DEV) for q in qs]
+
+    def step():
+        for layer in range(2):
+            cache.decode_tokens(layer, qs[layer], out=outs[layer], lse=lses[layer])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs], [x.clone() for x in lses]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer in range(2):
+            assert torch.equal(outs[layer], eager[0][layer]), (rep, layer)
+            assert torch.equal(lses[layer], eager[1][layer]), (rep, layer)
+        step()
+        torch.cuda.synchronize()
+    cache.close()
