@@ -75,6 +75,9 @@ def main() -> int:
     ap.add_argument("--layout", default="combined",
                     choices=["combined", "stepwise", "contiguous", "nosync"],
                     help="cache layout the views follow (combined: the method's own)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer pools to rotate through (0: the workload's own count; 1 keeps one "
+                         "layer's K/V resident in the last-level cache)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the whole step captured as one HIP graph (workloads "
                          "whose views do not change between steps)")
@@ -101,7 +104,8 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     total_steps = args.warmup + 2 * args.steps + 1
     grows = args.workload == "w8_32k"
-    wl = W.make(args.workload, steps=total_steps if grows else 0)
+    extra = {"n_layers": args.layers} if args.layers > 0 else {}
+    wl = W.make(args.workload, steps=total_steps if grows else 0, **extra)
     n, hq, hkv, d, L = wl.n_workers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers
     kv_dt = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
     elem = 2 if wl.kv_dtype == "bf16" else 4
