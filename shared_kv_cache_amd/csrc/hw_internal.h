@@ -77,7 +77,7 @@ struct DecodeArgs {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t group;           // n_q_heads / n_kv_heads
-  int32_t rows;            // n_workers * group
+  int32_t rows;            // stacked rows per KV head: n_workers * n_new * group
   int32_t n_splits;
   int32_t page_groups;
   int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)

@@ -2,7 +2,7 @@
 //
 //   rope_append          RoPE-on-insert of new tokens at block-local positions
 //                        [Hogwild! Inference paper summary, s5 steps 1-2; s9]
-//   concurrent_decode    split-K attention of every (worker, query head) row of one KV head
+//   concurrent_decode    split-K attention of every (worker, [query token,] query head) row of one KV head
 //                        over a balanced range of 32-token groups, rotating each worker's
 //                        query once per block it enters [summary s5 steps 3-5; s9 kernel]
 //   lse_merge            log-sum-exp merge of the split partials [summary s9 "partial
@@ -11,8 +11,9 @@
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16; v_mfma_f32_16x16x4_f32 for fp32 pools):
 //   scores   S^T[token slot, row] = K[slot, :] . Qrot^T[:, row]    A = K tile, B = Qrot
 //   output   O^T[d, row]         += V^T[d, token] . P^T[token, row] A = V tile, B = P
-// Rows are (worker, query head of the KV head) pairs stacked 16 per tile, so one K/V byte
-// read from HBM serves every worker and every query head of its group. Both products keep
+// Rows are (worker, query head of the KV head) pairs, or (worker, query token, head) with
+// several query tokens per worker, stacked 16 per tile, so one K/V byte read from HBM serves
+// every worker and every query head of its group. Both products keep
 // the row index in the MFMA N dimension, so one lane owns one row in S, P and O and the
 // softmax needs only two cross-lane exchanges per 32 tokens. The pool layouts (hogwild.h)
 // put each lane's 16-byte operand at lane * 16 of a 1 KiB run, so every load is coalesced
