@@ -3,6 +3,10 @@
 Usage: ``python -m shared_kv_cache_amd.build`` (or ``__graft_entry__.build()``).
 Always recompiles. The library exports the C ABI of ``include/hogwild.h`` and
 ``include/hogwild_debug.h``.
+
+``--asan-host OUT``: build a copy at OUT whose host code (not the device code) carries
+AddressSanitizer, for the CPU tests of the host logic; load it with the sanitizer runtime
+preloaded (``clang -print-file-name=libclang_rt.asan-x86_64.so``).
 """
 
 from __future__ import annotations
@@ -28,10 +32,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+ASAN_HOST = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = True, out: str = LIB, extra=()) -> str:
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,10 +48,13 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) == 3 and sys.argv[1] == "--asan-host":
+        build(verbose=True, out=os.path.abspath(sys.argv[2]), extra=ASAN_HOST)
+    else:
+        build(verbose=True)
     sys.exit(0)
