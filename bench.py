@@ -251,7 +251,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, args.layout, kq)
-    traffic = read_traffic(wl.name)
+    # the committed counters were taken on the default configuration of each workload
+    default_cfg = (kq == 1 and args.layout == "combined" and not args.splits and not args.layers
+                   and not args.graph)
+    traffic = read_traffic(wl.name) if default_cfg else None
 
     line = {
         "metric": METRIC, "value": round(worker_steps, 3), "unit": "worker-steps/s",
