@@ -370,10 +370,10 @@ def test_split_choice_and_override(ctx):
     _fill(ctx, 0, {0: 900, 1: 24})
     H.hw_set_views(ctx, [[0, 1]])
     auto = H.hw_debug_resolve(ctx, 0, 1)["n_splits"]
-    # 30 groups: min(3/4 of 256 CUs / (2 KV heads * 1 row block), 30 // 8) without a GPU
-    assert auto == 3
-    H.hw_set_split(ctx, 7)
-    assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == 7
+    # 30 groups: min(3/4 of 256 CUs / (2 KV heads * 1 row block), 30 // 4) without a GPU
+    assert auto == 7
+    H.hw_set_split(ctx, 5)
+    assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == 5
     with pytest.raises(H.HwError):
         H.hw_set_split(ctx, 257)
     H.hw_set_split(ctx, 0)
