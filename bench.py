@@ -230,7 +230,9 @@ def main() -> int:
     dec_ms = H.hw_debug_kernel_elapsed(cache.ctx)
     H.hw_debug_kernel_events(cache.ctx, 0)
     res = H.hw_debug_resolve(cache.ctx, 0, n)
-    n_splits = res["n_splits"]
+    # the resolver reports the one-token choice; several tokens per worker use more row
+    # blocks and so fewer partitions
+    n_splits = res["n_splits"] if kq == 1 else None
 
     # Algorithmic bytes: every K and V byte of the union of the views once per layer,
     # plus q read and out / lse written.
