@@ -182,8 +182,9 @@ hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new,
 hw_status hw_reset_block(hw_ctx *ctx, int32_t block_id);
 
 /* Force the number of KV partitions per head for following decodes (1 .. max_splits), or
- * 0 for the automatic choice (workgroups for about three quarters of the compute units, each
- * partition of >= 8 token groups). */
+ * 0 for the automatic choice: workgroups for about three quarters of the compute units (all
+ * of them with several query tokens per worker), at least 4 token groups a partition, and a
+ * single partition for heads of at most 16 groups. */
 hw_status hw_set_split(hw_ctx *ctx, int32_t n_splits);
 
 /* Introspection: a block's length in a layer and its page ids in order (at most cap are
