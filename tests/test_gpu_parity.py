@@ -55,7 +55,7 @@ def test_tiny_fp32_parity():
     cache.close()
 
 
-@pytest.mark.parametrize("page_size", [32, 256])
+@pytest.mark.parametrize("page_size", [32, 256, 8192])   # 8192: the largest page the library takes
 def test_tiny_fp32_page_sizes_and_splits(page_size):
     wl = W.make("tiny_fp32", page_size=page_size)
     cache = make_cache(wl)
