@@ -186,15 +186,14 @@ def test_many_rows_multiple_row_blocks_and_empty_view():
 
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("n_workers,group", [(2, 8), (4, 8), (5, 8), (8, 8), (3, 5), (6, 8),
-                                             (7, 6), (16, 2), (9, 7), (32, 2), (64, 1), (13, 5)])
+                                             (7, 6), (16, 2), (9, 7), (32, 2), (64, 1), (13, 5),
+                                             (128, 2)])
 def test_every_bf16_kernel_variant(head_dim, n_workers, group):
     # 15 to 65 rows per KV head: one to four 16-row tiles, i.e. the 8-wave single-stage
-    # kernels and the 4-wave two-stage kernels, each under automatic and forced KV
-    # partitions (several rotation phases at one partition). Up to 8 workers per block of
-    # rows share one cos/sin table per (worker, block); 9 to 64 workers (groups of 1, 2, 5, 7)
-    # take the per-row rotation, and 13 workers of 5 heads mix both in one launch.
-    # Partition counts: automatic, 1, 3, 40 and 80 (bounds chosen by the host; many
-    # partitions empty at 80).
+    # kernels (wide descriptors up to 6 workers, narrow beyond) and the 4-wave two-stage
+    # kernels; 128 workers of 2 heads make 256 rows, four row blocks of the 4-wave kernel.
+    # Each under automatic and forced KV partitions: 1 (several rotation phases in one
+    # workgroup), 3, 40 and 80 (bounds chosen by the host; many partitions empty at 80).
     wl = variant_workload(head_dim, n_workers, group)
     cache = make_cache(wl, max_blocks=n_workers + 2, max_splits=128)
     fill_layer(cache, wl, 0)
