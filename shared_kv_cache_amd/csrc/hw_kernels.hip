@@ -812,13 +812,20 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // and the stage read completes before the refill. Group 0 is computed outside the loop
     // so that no loop iteration carries its register loads (whose waits would then drain
     // the stage in flight).
+    // A wave raises its priority while it takes its group from the stage and issues the next
+    // fill, and drops it to compute: the other wave on the SIMD, mid-compute, then yields
+    // the issue slots to the one whose data has landed, which keeps the fills going.
+    __builtin_amdgcn_s_setprio(1);
     if (wcount > 1) {
       const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
       F::load_lds(kl + gb, vl + gb, lane, stage);
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if (wcount > 0) process(st, 0, dl_cur);
     for (long long i = 1; i < wcount; ++i) {
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // group i's fill has landed
       st.f.stage_read(stage, lane);
       st.desc_x = next.x;
@@ -829,6 +836,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         const size_t gb = ((size_t)next2.x + head_groups) * (size_t)(32 * D);
         F::load_lds(kl + gb, vl + gb, lane, stage);
       }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
       next = next2;
       ow = ow_next;
       ow_next = ow_next2;
