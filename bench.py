@@ -2,19 +2,22 @@
 """Benchmark of the Hogwild! concurrent-attention decode step on one MI355X.
 
 A step is one decode step of every worker over every layer the workload times
-(for w8_32k each layer first appends one new token per worker). Inputs are
-seeded synthetic tensors already resident in HBM when the timed region starts.
-With --query-tokens K > 1 every worker queries K tokens per step together
-(hw_concurrent_decode_tokens: a paragraph header's tokens, causal), over the
-same cache.
+(for w8_32k each layer first appends one new token per worker: under a step
+plan by default, hw_append_step + hw_concurrent_decode, optionally replayed as
+one HIP graph). Inputs are seeded synthetic tensors already resident in HBM
+when a timed region starts. With --query-tokens K > 1 every worker queries K
+tokens per step together (hw_concurrent_decode_tokens, causal).
 
-Prints ONE JSON line: worker-steps/s (value), the step's ideal-bytes GB/s,
-a roofline object for the dominant kernel (concurrent_decode: algorithmic
-bytes per launch / its average duration, from start/stop HIP events that the
-kernel's own dispatch records on its stream during a timed pass), the measured
-streaming-read ceiling of the same GPU (a plain 16-byte streaming-read kernel
-at the decode launch's byte count and at 512 MiB, fresh memory each launch)
-and the fp64 oracle's CPU rate on a bounded sample of the same workload.
+Prints ONE JSON line. The headline workload (default w4_16k) gives `value`
+(worker-steps/s) and `ms_per_step`: the median over --repeats timed regions of
+--steps steps each, with the spread beside it. A second workload (default
+w8_32k, the 8-worker case with appends) is timed the same way and reported
+under its own key. Each carries a roofline object for the dominant kernel
+(concurrent_decode: algorithmic bytes per launch / its average duration, from
+start/stop HIP events that the kernel's own dispatch records on its stream
+during a timed pass), the measured streaming-read ceiling of the same GPU and
+the fp64 oracle's CPU rate on one full step of the same workload (one process
+per host core, in a child process that never touches the GPU).
 """
 
 from __future__ import annotations
@@ -24,6 +27,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "concurrent-attn decode worker-steps/s and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "shared_kv_cache_amd", "csrc", "hw_kernels.hip")
+WORKLOADS = ["tiny_fp32", "w2_4k", "w4_16k", "w8_32k", "w4_128k_sinks"]
 
 
 def log(*a):
@@ -59,65 +64,31 @@ def read_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w4_16k",
-                    choices=["tiny_fp32", "w2_4k", "w4_16k", "w8_32k", "w4_128k_sinks"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 1 GiB copy kernel (counter calibration)")
-    ap.add_argument("--splits", type=int, default=0, help="force KV partitions per head")
-    ap.add_argument("--layout", default="combined",
-                    choices=["combined", "stepwise", "contiguous", "nosync"],
-                    help="cache layout the views follow (combined: the method's own)")
-    ap.add_argument("--layers", type=int, default=0,
-                    help="layer pools to rotate through (0: the workload's own count; 1 keeps one "
-                         "layer's K/V resident in the last-level cache)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of the whole step captured as one HIP graph (workloads "
-                         "whose views do not change between steps)")
-    ap.add_argument("--query-tokens", type=int, default=1,
-                    help="query tokens per worker and step (several: one causal decode of all)")
-    args = ap.parse_args()
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the concurrent-"
-              "attention step here is single-GPU by design", file=sys.stderr)
-        return 2
 
-    if args.query_tokens < 1:
-        print("--query-tokens must be at least 1", file=sys.stderr)
-        return 2
-
+def run_gpu(name, args, graph, plan):
+    """Time one workload on cuda:0. Returns the measured figures (no JSON formatting)."""
     import numpy as np
     import torch
 
     from shared_kv_cache_amd import hogwild as H
     from shared_kv_cache_amd import workloads as W
 
-    torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    total_steps = args.warmup + 2 * args.steps + 1
-    grows = args.workload == "w8_32k"
+    kq = args.query_tokens
+    grows = name == "w8_32k"
+    plan = plan and grows and kq == 1
+    steps, reps = args.steps, args.repeats
+    # planned window: warm-up, the timed repeats, the kernel-event pass, graph warm-up
+    total_steps = args.warmup + reps * steps + steps + 4
     extra = {"n_layers": args.layers} if args.layers > 0 else {}
-    wl = W.make(args.workload, steps=total_steps if grows else 0, **extra)
+    wl = W.make(name, steps=total_steps if grows else 0, **extra)
     n, hq, hkv, d, L = wl.n_workers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers
     kv_dt = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
     elem = 2 if wl.kv_dtype == "bf16" else 4
-
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        log("copy calibration: 3 x torch.mul(src, 1.0, out=dst), 1 GiB read + 1 GiB written each")
 
     t0 = time.time()
     cache = H.HogwildCache(
@@ -125,7 +96,7 @@ def main() -> int:
         n_pages=wl.n_pages, max_blocks=len(wl.blocks()) + 1, max_workers=n,
         max_position=wl.max_position, kv_dtype=wl.kv_dtype, page_seed=wl.page_seed,
         rope_theta=wl.theta, max_splits=512 if args.splits > 256 else 0,
-        max_query_tokens=args.query_tokens, device="cuda:0")
+        max_query_tokens=kq, device="cuda:0")
     blocks = wl.blocks()
 
     def gen(layer):
@@ -140,156 +111,163 @@ def main() -> int:
     cache.set_views(wl.views(args.layout))
     if args.splits:
         H.hw_set_split(cache.ctx, args.splits)
-    kq = args.query_tokens
-    n_q_steps = total_steps if grows and kq == 1 else 1
-
-    def q_host(layer, s):
-        return wl.q(layer, s) if kq == 1 else wl.q_tokens(layer, kq)
-
-    q_dev = [[torch.from_numpy(q_host(layer, s if grows else 0)).to(dev) for s in range(n_q_steps)]
+    if plan:
+        cache.plan_steps(total_steps, wl.inprogress, [1] * n)
+    # Inputs in fixed device buffers, per layer: the queries and (growing workloads) the
+    # step's new token of every worker, as a model's projections would leave them.
+    q_dev = [torch.from_numpy(wl.q(layer) if kq == 1 else wl.q_tokens(layer, kq)).to(dev)
              for layer in range(L)]
     step_kv = None
-    if grows:   # one new token per worker per layer per step, pre-staged in HBM
-        step_kv = [[tuple(torch.from_numpy(x).to(dev).to(kv_dt) for x in wl.step_kv(layer, s + 1))
-                    for s in range(total_steps)] for layer in range(L)]
+    if grows:
+        step_kv = [tuple(torch.from_numpy(x).to(dev).to(kv_dt) for x in wl.step_kv(layer, 1))
+                   for layer in range(L)]
     outs = [torch.empty((n, kq, hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
     lses = [torch.empty((n, kq, hq), dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
-    log(f"setup {time.time() - t0:.1f}s: {wl.name}, {L} layers, T={wl.total_tokens()}")
+    log(f"setup {time.time() - t0:.1f}s: {wl.name}, {L} layers, T={wl.total_tokens()}"
+        f"{', step plan' if plan else ''}")
 
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    state = {"step": 0}
+    cur = {"stream": torch.cuda.current_stream(dev).cuda_stream}
 
     def step():
-        s = state["step"]
+        stream = cur["stream"]
         for layer in range(L):
             if grows:
-                k, v = step_kv[layer][s]
-                H.hw_append_kv(cache.ctx, layer, wl.inprogress, [1] * n, k.data_ptr(),
-                               v.data_ptr(), stream)
-            q = q_dev[layer][s if n_q_steps > 1 else 0]
+                k, v = step_kv[layer]
+                if plan:
+                    H.hw_append_step(cache.ctx, layer, k.data_ptr(), v.data_ptr(), stream)
+                else:
+                    H.hw_append_kv(cache.ctx, layer, wl.inprogress, [1] * n, k.data_ptr(),
+                                   v.data_ptr(), stream)
             if kq == 1:
-                H.hw_concurrent_decode(cache.ctx, layer, q.data_ptr(), outs[layer].data_ptr(),
-                                       lses[layer].data_ptr(), stream)
+                H.hw_concurrent_decode(cache.ctx, layer, q_dev[layer].data_ptr(),
+                                       outs[layer].data_ptr(), lses[layer].data_ptr(), stream)
             else:
-                H.hw_concurrent_decode_tokens(cache.ctx, layer, kq, q.data_ptr(),
+                H.hw_concurrent_decode_tokens(cache.ctx, layer, kq, q_dev[layer].data_ptr(),
                                               outs[layer].data_ptr(), lses[layer].data_ptr(), stream)
-        state["step"] = s + 1
 
-    def tokens_now():
-        return sum(H.hw_block_info(cache.ctx, b, 0)[0] for b in blocks)
+    done = {"steps": 0}
 
-    for _ in range(args.warmup):
-        step()
+    def run_steps(k):
+        for _ in range(k):
+            if g is not None:
+                g.replay()
+            else:
+                step()
+        done["steps"] += k
+
+    g = None
+    run_steps(args.warmup)
     torch.cuda.synchronize()
-    graph = None
-    if args.graph:
-        if grows:
-            print("--graph needs a workload whose views stay the same between steps", file=sys.stderr)
-            return 2
-        # The tables of the views are uploaded by the warm-up steps; the captured step holds
-        # only the decode and merge launches of every layer.
-        graph = torch.cuda.CUDAGraph()
+    if graph:
+        if grows and not plan:
+            raise SystemExit("--graph on a growing workload needs the step plan (drop --no-plan)")
+        # Capture one step; growing workloads take their positions from the plan's counters.
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            stream = side.cuda_stream
-            step()
-        torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            stream = torch.cuda.current_stream(dev).cuda_stream
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            cur["stream"] = side.cuda_stream
             step()
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        for _ in range(2):
-            graph.replay()
+        cur["stream"] = torch.cuda.current_stream(dev).cuda_stream
+        torch.cuda.synchronize()
+        run_steps(2)
         torch.cuda.synchronize()
 
-    # Timed region 1: headline wall clock, no instrumentation.
+    def tokens_now():
+        # under a plan the host's lengths stay at the plan's start; the device has appended
+        # one token per worker and layer per step since
+        base = sum(H.hw_block_info(cache.ctx, b, 0)[0] for b in blocks)
+        return base + (n * done["steps"] if plan else 0)
+
+    # Timed regions: `reps` regions of `steps` steps each, uninstrumented.
     t_tok0 = tokens_now()
+    ms = []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        run_steps(steps)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms.append(ev0.elapsed_time(ev1))
     t_tok1 = tokens_now()
-    log(f"timed: {args.steps} steps in {ms_total:.3f} ms")
-
-    # Timed region 2: the same steps, the decode kernels recording start/stop events.
-    H.hw_debug_kernel_events(cache.ctx, args.steps * L)
+    # Kernel pass: the same steps run eagerly, the decode kernels recording start/stop events.
+    gsave, g = g, None
+    H.hw_debug_kernel_events(cache.ctx, steps * L)
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step()
+    run_steps(steps)
     torch.cuda.synchronize()
     dec_ms = H.hw_debug_kernel_elapsed(cache.ctx)
     H.hw_debug_kernel_events(cache.ctx, 0)
-    res = H.hw_debug_resolve(cache.ctx, 0, n)
-    # the resolver reports the one-token choice; several tokens per worker use more row
-    # blocks and so fewer partitions
-    n_splits = res["n_splits"] if kq == 1 else None
+    t_tok2 = tokens_now()
+    g = gsave
+    n_splits = H.hw_debug_resolve(cache.ctx, 0, n)["n_splits"] if kq == 1 else None
+    if plan:
+        cache.plan_end()
+    cache.close()
+    del cache, g
+    torch.cuda.synchronize()
 
-    # Algorithmic bytes: every K and V byte of the union of the views once per layer,
-    # plus q read and out / lse written.
+    med = pct(ms, 0.5) / steps
     avg_tokens = 0.5 * (t_tok0 + t_tok1) if grows else float(wl.total_tokens())
-    kv_bytes = avg_tokens * hkv * d * 2 * elem
+    kern_tokens = 0.5 * (t_tok1 + t_tok2) if grows else float(wl.total_tokens())
     io_bytes = n * kq * (hq * d * 4 * 2 + hq * 4)
-    launch_bytes = kv_bytes + io_bytes
+    launch_bytes = avg_tokens * hkv * d * 2 * elem + io_bytes
+    kern_launch_bytes = kern_tokens * hkv * d * 2 * elem + io_bytes
     append_bytes = (n * hkv * d * elem * 2 * 2) if grows else 0   # read + write new K and V
     step_bytes = L * (launch_bytes + append_bytes)
-    ms_step = ms_total / args.steps
-    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     dec_avg = float(np.mean(dec_ms))
-    achieved = launch_bytes / (dec_avg * 1e-3) / 1e9
-    worker_steps = n * args.steps / (ms_total * 1e-3)
-
-    stream_read = stream_ceiling(torch, H, dev, [int(launch_bytes), 512 << 20])
-    cache.close()
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, args.layout, kq)
-    # the committed counters were taken on the default configuration of each workload
-    default_cfg = (kq == 1 and args.layout == "combined" and not args.splits and not args.layers
-                   and not args.graph)
-    traffic = read_traffic(wl.name) if default_cfg else None
-
-    line = {
-        "metric": METRIC, "value": round(worker_steps, 3), "unit": "worker-steps/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
-        "config": {
-            "workload": wl.name, "layout": args.layout, "workers": n, "q_heads": hq,
-            "kv_heads": hkv, "head_dim": d,
-            "layers": L, "tokens_per_layer": round(avg_tokens, 1), "kv_dtype": wl.kv_dtype,
-            "page_size": wl.page_size, "splits_per_head": n_splits,
-            "step_ideal_bytes": int(step_bytes), "step_GBps": round(step_gbps, 1),
-            "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-            "decode_kernel_us": round(dec_avg * 1e3, 3),
-            "appends_per_step": L if grows else 0, "query_tokens": kq, "hip_graph": graph is not None,
-        },
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-        },
-        "stream_read": stream_read,
-        "cpu_baseline": cpu,
+    return {
+        "wl": wl, "plan": plan, "graph": graph, "ms_step": med,
+        "spread": {"repeats": reps, "steps_per_repeat": steps,
+                   "ms_per_step_min": round(min(ms) / steps, 5),
+                   "ms_per_step_p10": round(pct(ms, 0.1) / steps, 5),
+                   "ms_per_step_p90": round(pct(ms, 0.9) / steps, 5),
+                   "ms_per_step_max": round(max(ms) / steps, 5)},
+        "worker_steps": n / (med * 1e-3), "avg_tokens": avg_tokens,
+        "step_bytes": step_bytes, "launch_bytes": kern_launch_bytes, "dec_avg_ms": dec_avg,
+        "achieved": kern_launch_bytes / (dec_avg * 1e-3) / 1e9, "n_splits": n_splits,
+        "elem": elem,
     }
-    print(json.dumps(line), flush=True)
-    return 0
 
 
-def stream_ceiling(torch, H, dev, sizes, reps=10):
+def describe(r, args, layout):
+    """Config and roofline objects of one run_gpu result."""
+    wl = r["wl"]
+    step_gbps = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    default_cfg = (args.query_tokens == 1 and layout == "combined" and not args.splits
+                   and not args.layers)
+    traffic = read_traffic(wl.name) if default_cfg else None
+    config = {
+        "workload": wl.name, "layout": layout, "workers": wl.n_workers, "q_heads": wl.n_q_heads,
+        "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "layers": wl.n_layers,
+        "tokens_per_layer": round(r["avg_tokens"], 1), "kv_dtype": wl.kv_dtype,
+        "page_size": wl.page_size, "splits_per_head": r["n_splits"],
+        "step_ideal_bytes": int(r["step_bytes"]), "step_GBps": round(step_gbps, 1),
+        "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "decode_kernel_us": round(r["dec_avg_ms"] * 1e3, 3),
+        "per_layer_other_us": round(r["ms_step"] * 1e3 / wl.n_layers - r["dec_avg_ms"] * 1e3, 3),
+        "appends_per_step": wl.n_layers if wl.name == "w8_32k" else 0,
+        "query_tokens": args.query_tokens, "hip_graph": r["graph"], "step_plan": r["plan"],
+    }
+    roofline = {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4),
+                "traffic": traffic}
+    return config, roofline
+
+
+def stream_ceiling(sizes, reps=10):
     """Streaming-read ceiling: the library's plain read probe (16-byte streaming loads,
     every byte read once) over fresh windows of a 1 GiB buffer, so that no launch re-reads
     what the 256 MB last-level cache may still hold; median of `reps` launches timed by
     events of the kernel's own dispatch, best of two grid sizes."""
+    import torch
+
+    from shared_kv_cache_amd import hogwild as H
+
+    dev = torch.device("cuda", 0)
     total = 1 << 30
     buf = torch.ones(total // 4, dtype=torch.float32, device=dev)
     sink = torch.zeros(1 << 14, dtype=torch.float32, device=dev)
@@ -317,55 +295,178 @@ def stream_ceiling(torch, H, dev, sizes, reps=10):
     return {"kernel": "stream_read_kernel via hw_debug_stream_read", "points": points}
 
 
-def cpu_baseline(wl, target_s: float, layout: str = "combined", query_tokens: int = 1):
-    """The fp64 oracle, as it stands, on the host cores: whole layers of the workload
-    (all workers, all query heads) until about target_s seconds have passed, with numpy's
-    BLAS on every core this process may use; then one layer on one thread."""
+# ------------------------------------------------------------------ CPU baseline
+
+def _oracle_layer(job):
+    """One layer of the oracle on one thread (a pool worker): (layer, seconds of oracle time).
+    The inputs are drawn before the clock starts."""
+    name, layer, layout, kq, n_layers = job
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import hogwild_oracle as O
+    from shared_kv_cache_amd import workloads as W
 
-    threads = len(os.sched_getaffinity(0))
-    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
-        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    wl = W.make(name, n_layers=n_layers)
+    with threadpool_limits(limits=1):
+        blocks = {b: tuple(x.astype(np.float64) for x in wl.kv(layer, b)) for b in wl.blocks()}
+        q = (wl.q(layer) if kq == 1 else wl.q_tokens(layer, kq)).astype(np.float64)
+        t0 = time.perf_counter()
+        O.concurrent_attention(q, blocks, wl.views(layout), theta=wl.theta)
+        return layer, time.perf_counter() - t0
+
+
+def cpu_baseline_child(name, layout, kq, procs):
+    """Runs in a child process that never touches the GPU: the fp64 oracle, as it stands, on
+    one full step of the workload (every layer, worker and query head), layer l on pool
+    process l mod procs, each process single-threaded; the step's time is the busiest
+    process's total. Then one layer alone on one thread."""
+    import multiprocessing as mp
+
+    from shared_kv_cache_amd import workloads as W
+
+    wl = W.make(name)
+    L = wl.n_layers
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
+    one = _oracle_layer((name, 0, layout, kq, L))[1]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(processes=procs) as pool:
+        res = pool.map(_oracle_layer, [(name, layer, layout, kq, L) for layer in range(L)],
+                       chunksize=1)
+    wall = time.perf_counter() - t0
+    busy = [0.0] * procs
+    for layer, sec in res:
+        busy[layer % procs] += sec
+    step_s = max(busy)
+    rate = wl.n_workers / step_s
+    return {"value": round(rate, 5), "unit": "worker-steps/s", "cores": procs, "kind": "oracle",
+            "sample": f"one full step of {name}: all {L} layers, {wl.n_workers} workers "
+                      f"({kq} query token(s) each), {wl.n_q_heads} query heads; fp64 numpy "
+                      f"oracle, layer l on process l mod {procs}, one BLAS thread each; step time "
+                      f"= the busiest process's oracle seconds ({step_s:.2f} s; pool wall "
+                      f"{wall:.2f} s including input draws)",
+            "cpu_model": model, "single_thread_s_per_layer": round(one, 3),
+            "step_seconds": round(step_s, 3)}
 
-    def layer_inputs(layer):
-        blocks = {b: tuple(x.astype(np.float64) for x in wl.kv(layer, b)) for b in wl.blocks()}
-        q = wl.q(layer) if query_tokens == 1 else wl.q_tokens(layer, query_tokens)
-        return blocks, q.astype(np.float64)
 
-    done, t_sum = 0, 0.0
-    with threadpool_limits(limits=threads):
-        for layer in range(wl.n_layers):
-            blocks, q = layer_inputs(layer)
-            t0 = time.perf_counter()
-            O.concurrent_attention(q, blocks, wl.views(layout), theta=wl.theta)
-            t_sum += time.perf_counter() - t0
-            done += 1
-            if t_sum >= target_s:
-                break
-    with threadpool_limits(limits=1):
-        blocks, q = layer_inputs(0)
-        t0 = time.perf_counter()
-        O.concurrent_attention(q, blocks, wl.views(layout), theta=wl.theta)
-        one = time.perf_counter() - t0
-    per_layer = t_sum / done
-    rate = wl.n_workers / (per_layer * wl.n_layers)
-    log(f"cpu oracle: {done} layers in {t_sum:.2f}s on {threads} threads -> {rate:.4f} "
-        f"worker-steps/s; one layer on 1 thread {one:.2f}s")
-    return {"value": round(rate, 5), "unit": "worker-steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {wl.n_layers} layers at step 0, all {wl.n_workers} workers "
-                      f"({query_tokens} query token(s) each) and "
-                      f"{wl.n_q_heads} query heads; fp64 numpy oracle, BLAS on {threads} threads; "
-                      f"rate = workers / (mean seconds per layer x {wl.n_layers} layers)",
-            "cpu_model": model, "single_thread_s_per_layer": round(one, 3)}
+def cpu_baseline(name, layout, kq):
+    procs = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        procs = min(procs, int(os.environ["OMP_NUM_THREADS"]))
+    procs = max(1, min(procs, 16))
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", name,
+           "--layout", layout, "--query-tokens", str(kq), "--cpu-procs", str(procs)]
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    t0 = time.time()
+    out = subprocess.run(cmd, capture_output=True, text=True, env=env, timeout=900)
+    if out.returncode != 0:
+        log(out.stderr[-2000:])
+        raise RuntimeError(f"cpu baseline child failed ({out.returncode})")
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    log(f"cpu oracle {name}: {res['value']} worker-steps/s on {res['cores']} processes "
+        f"({time.time() - t0:.1f}s)")
+    return res
+
+
+# ------------------------------------------------------------------ main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="steps per timed region")
+    ap.add_argument("--repeats", type=int, default=20, help="timed regions; the median is reported")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="w4_16k", choices=WORKLOADS)
+    ap.add_argument("--extra-workload", default="w8_32k", choices=WORKLOADS + ["none"],
+                    help="a second workload timed in the same run, reported under its own key")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB copy kernel (counter calibration)")
+    ap.add_argument("--splits", type=int, default=0, help="force KV partitions per head")
+    ap.add_argument("--layout", default="combined",
+                    choices=["combined", "stepwise", "contiguous", "nosync"],
+                    help="cache layout the views follow (combined: the method's own)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer pools to rotate through (0: the workload's own count; 1 keeps one "
+                         "layer's K/V resident in the last-level cache)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the whole step captured as one HIP graph")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="growing workloads: host-planned appends (hw_append_kv) instead of a step plan")
+    ap.add_argument("--query-tokens", type=int, default=1,
+                    help="query tokens per worker and step (several: one causal decode of all)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-procs", type=int, default=1, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+
+    if args.cpu_baseline_child:
+        print(json.dumps(cpu_baseline_child(args.workload, args.layout, args.query_tokens,
+                                            args.cpu_procs)), flush=True)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the concurrent-"
+              "attention step here is single-GPU by design", file=sys.stderr)
+        return 2
+    if args.query_tokens < 1 or args.steps < 1 or args.repeats < 1:
+        print("--query-tokens, --steps and --repeats must be at least 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 x torch.mul(src, 1.0, out=dst), 1 GiB read + 1 GiB written each")
+
+    plan = not args.no_plan
+    head = run_gpu(args.workload, args, args.graph, plan)
+    log(f"{args.workload}: median {head['ms_step']:.4f} ms/step over {args.repeats} x "
+        f"{args.steps} steps; decode kernel {head['dec_avg_ms'] * 1e3:.2f} us")
+    extra = None
+    if args.extra_workload != "none" and args.extra_workload != args.workload:
+        # the second workload in its own best configuration: growing ones under a step plan,
+        # replayed as one HIP graph
+        grows = args.extra_workload == "w8_32k"
+        extra = run_gpu(args.extra_workload, args, grows and plan, plan)
+        log(f"{args.extra_workload}: median {extra['ms_step']:.4f} ms/step; decode kernel "
+            f"{extra['dec_avg_ms'] * 1e3:.2f} us")
+    stream_read = stream_ceiling([int(head["launch_bytes"]), 512 << 20])
+    cpu = cpu_extra = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.layout, args.query_tokens)
+        if extra is not None:
+            cpu_extra = cpu_baseline(args.extra_workload, args.layout, args.query_tokens)
+
+    config, roofline = describe(head, args, args.layout)
+    line = {
+        "metric": METRIC, "value": round(head["worker_steps"], 3), "unit": "worker-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": head["wl"].kv_dtype, "data": "synthetic",
+        "config": config, "spread": head["spread"], "roofline": roofline,
+        "stream_read": stream_read, "cpu_baseline": cpu,
+    }
+    if extra is not None:
+        xc, xr = describe(extra, args, args.layout)
+        line[extra["wl"].name] = {
+            "value": round(extra["worker_steps"], 3), "unit": "worker-steps/s",
+            "ms_per_step": round(extra["ms_step"], 5), "spread": extra["spread"],
+            "config": xc, "roofline": xr, "cpu_baseline": cpu_extra,
+        }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 if __name__ == "__main__":

@@ -31,6 +31,22 @@
  * hw_append_kv and hw_concurrent_decode; ordering between appends, decodes and page reuse
  * relies on that stream's order. Device faults surface at the caller's next synchronisation.
  *
+ * Graph capture (HIP stream capture, e.g. torch.cuda.graph): a decode launches kernels only,
+ * except when the views' device tables must be uploaded first (views set since the last
+ * upload, or lengths of the views' blocks changed by appends or resets): then it copies
+ * from pinned staging, which capture cannot hold, so during a capture it returns
+ * HW_ERR_INVALID_ARG and enqueues nothing. Capture decodes after an eager decode with the
+ * same views and lengths has uploaded the tables. Replays read the tables in the workspace
+ * and are valid until the next upload (the next eager decode after the views or lengths
+ * change); the split partials in the workspace are shared by every decode of the context,
+ * so replays and eager work on the context must stay ordered on one stream. hw_append_kv
+ * captures as kernels, but the host advances the blocks' lengths at capture time, not at
+ * replay, so a captured append is replayed into the same slots: for steps that grow the
+ * cache, capture under a step plan (hw_plan_steps below), whose appends and decodes take
+ * their positions from device-side counters. No call records a memset node. hw_set_views
+ * is host-only (nothing to order on a stream, hence no stream argument): it takes effect at
+ * the next decode's upload.
+ *
  * Errors: every call returns hw_status. Arguments and state are validated before anything
  * is mutated or enqueued: on any error other than HW_ERR_HIP nothing was enqueued and the
  * context is unchanged. HW_ERR_HIP reports a failed HIP call (a launch or a copy); the
@@ -84,7 +100,9 @@ typedef struct {
    *   V element (u, i) at (((i/16)*4 + u/8)*16 + i%16)*8 + u%8
    * so that every 64-lane, 16-byte-per-lane load of the decode kernel reads 1 KiB of
    * contiguous memory straight into the matrix-core operand layout. K holds rotated keys,
-   * V raw values. Slots of the pool that no block's token occupies are never read. */
+   * V raw values. The decode reads whole 32-token groups; the slots of a group that no token
+   * occupies are masked out (their scores dropped, their values zeroed before use), so the
+   * pools need no initialisation and may hold any bits, NaN included. */
   void *k_pool;
   void *v_pool;
 } hw_config;
@@ -115,8 +133,10 @@ size_t hw_workspace_bytes(const hw_ctx *ctx);
 
 /* Hand the context a device workspace of at least hw_workspace_bytes() bytes (256-byte
  * aligned, caller-owned, must outlive every call that uses it). Computes the cos/sin table
- * on the host and copies it synchronously; this is setup, not a step.
- * Errors: HW_ERR_WORKSPACE if too small or misaligned, HW_ERR_HIP on a copy failure. */
+ * on the host and copies it synchronously, and allocates the context's pinned staging ring
+ * for table uploads; this is setup, not a step: no later call allocates memory.
+ * Errors: HW_ERR_WORKSPACE if too small or misaligned, HW_ERR_HIP on a copy or allocation
+ * failure. */
 hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes);
 
 /* Append n_tokens[i] tokens to block block_ids[i] of one layer, for i < n_blocks
@@ -174,6 +194,59 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
  * max_query_tokens; HW_ERR_STALE_VIEW when a worker's first token would sit below 0. */
 hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
                                       float *out, float *lse, void *stream);
+
+/* ---- Step plans: a whole decode step, appends included, with no host work inside --------
+ * The pages' step (summary s8) is: every worker appends its token, the views are rebuilt,
+ * attention runs. Between two steps of one paragraph the views keep their blocks and only
+ * the lengths grow, so with default offsets every quantity a decode reads is affine in the
+ * number of steps taken: each block's length, each group's token count and each (worker,
+ * block) query offset (the sum of the lengths from that block to the end of the worker's
+ * view, minus one). A step plan resolves the views once for a window of n_steps steps and
+ * keeps, per layer, a device-side count of the planned appends done; hw_append_step
+ * advances it and the decode kernel derives the step's group sizes and offsets from it.
+ * A step (per layer: hw_append_step, then hw_concurrent_decode) then performs no host-side
+ * resolution, no staging wait and no copy: it can be captured once as a HIP graph and
+ * replayed for each step of the window.
+ *
+ * hw_plan_steps: block_ids[i] grows by tokens_per_step[i] tokens per step in every layer,
+ * for i < n_blocks (each id once; any other block of the views stays as it is). Needs
+ * bf16 pools, views set with default offsets and query positions (hw_set_views with NULL
+ * view_offsets and q_pos), and every block of the views and of the plan at the same length
+ * in every layer. Takes the pages of the whole window from the free list now, resolves the
+ * views' tables for the window (the groups the blocks will have at its end; a group's token
+ * count is clamped to 0..32 at each step), chooses the partitions as a decode would (or as
+ * hw_set_split forces), uploads the tables, zeroes the step counters and waits for the
+ * upload on `stream`. While a plan is active, hw_append_kv, hw_set_views, hw_reset_block,
+ * hw_set_workspace and hw_debug_reserve return HW_ERR_INVALID_ARG, decodes read the plan's
+ * tables, hw_concurrent_decode_tokens takes n_new = 1 only, and hw_block_info reports the
+ * lengths the blocks had when the plan began.
+ * Errors: HW_ERR_INVALID_ARG (a plan already active, fp32 pools, explicit offsets or q_pos,
+ * ids, counts, lengths that differ between layers, a block that would reach max_position),
+ * HW_ERR_STALE_VIEW (no views, or a view that would reach max_position within the window),
+ * HW_ERR_OUT_OF_PAGES, HW_ERR_WORKSPACE, HW_ERR_HIP; on any error nothing changed. Not
+ * capturable (it uploads and waits). */
+hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const int32_t *block_ids,
+                        const int32_t *tokens_per_step, void *stream);
+
+/* One planned step's append for one layer (summary s8: append before attention; s5 steps
+ * 1-2: stored once, RoPE'd at block-local positions). k, v: device [rows][n_kv_heads]
+ * [head_dim] bf16, raw, 16-byte aligned, rows = sum of tokens_per_step, in the plan's
+ * block order. Planned
+ * block i's tokens go to local positions base_i + s * tokens_per_step[i] + j, s being the
+ * number of planned appends this layer has had, written as hw_append_kv writes them; then
+ * the layer's count advances. One workgroup does the whole append (meant for a few tokens
+ * per step). An append past the window's n_steps writes nothing and is reported by
+ * hw_plan_end. Capturable: enqueues one kernel, reads nothing from the host.
+ * Errors: HW_ERR_INVALID_ARG (no plan, layer, NULL or misaligned k/v), HW_ERR_HIP. */
+hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, void *stream);
+
+/* End the active plan: waits for `stream`, reads the device's per-layer counts of planned
+ * appends back, sets every planned block's length in each layer to base + count *
+ * tokens_per_step, and returns the pages the blocks did not fill to the free list. Views
+ * and tables are then as without a plan (the next decode uploads fresh tables).
+ * Errors: HW_ERR_INVALID_ARG if no plan is active, or if some layer had more planned appends
+ * than n_steps (the extra appends were dropped; the plan is ended all the same); HW_ERR_HIP. */
+hw_status hw_plan_end(hw_ctx *ctx, void *stream);
 
 /* Return a block's pages to the free list and set its length to 0 in every layer, e.g. after
  * its step was committed and the worker starts a fresh block (summary s8). Pages are handed

@@ -66,6 +66,18 @@ struct Resolution {
   int64_t min_qpos = std::numeric_limits<int64_t>::max();
 };
 
+// A step plan (hw_plan_steps): blocks that grow by a fixed number of tokens per step in
+// every layer, over a window of steps, with the views' tables resolved once for the whole
+// window (affine in each layer's device-side count of planned appends).
+struct Plan {
+  bool active = false;
+  int32_t n_steps = 0;
+  std::vector<int32_t> blocks, tps, base;   // planned blocks, tokens per step, base lengths
+  int32_t rows = 0;                         // tokens per step over all planned blocks
+  int32_t n_workers = 0, n_groups = 0, splits = 1;
+  std::vector<int32_t> bounds;              // partition bounds (splits <= kMaxBoundSplits)
+};
+
 }  // namespace
 
 struct hw_ctx {
@@ -83,6 +95,10 @@ struct hw_ctx {
   size_t ws_bytes = 0;
   size_t off_trig = 0, off_freq = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0;
   size_t tables_bytes = 0;
+  // step-plan region: counters [n_layers] + overflow flag, block table, page lists,
+  // {d0, rate} offsets, 4-int group descriptors
+  size_t off_plan = 0, plan_cnt = 0, plan_blk = 0, plan_pages = 0, plan_delta = 0, plan_groups = 0;
+  Plan plan;
   size_t part_o_bytes = 0, part_lse_bytes = 0, total_bytes = 0;
 
   // upload cache
@@ -151,6 +167,19 @@ void layout_workspace(hw_ctx *c) {
   c->off_part_lse = off;
   c->part_lse_bytes = (size_t)g.max_splits * g.n_kv_heads * max_rows * sizeof(float);
   off = align_up(off + c->part_lse_bytes);
+  c->off_plan = off;
+  size_t po = 0;
+  c->plan_cnt = po;
+  po = align_up(po + ((size_t)g.n_layers + 1) * sizeof(int32_t));
+  c->plan_blk = po;
+  po = align_up(po + (size_t)g.max_blocks * 4 * sizeof(int32_t));
+  c->plan_pages = po;
+  po = align_up(po + (size_t)g.n_pages * sizeof(int32_t));
+  c->plan_delta = po;
+  po = align_up(po + (size_t)g.max_blocks * g.max_workers * 2 * sizeof(int32_t));
+  c->plan_groups = po;
+  po = align_up(po + max_groups * 4 * sizeof(int32_t));
+  off = align_up(off + po);
   c->total_bytes = off;
 }
 
@@ -545,6 +574,7 @@ size_t hw_workspace_bytes(const hw_ctx *ctx) { return ctx ? ctx->total_bytes : 0
 
 hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes) {
   if (!ctx) return HW_ERR_INVALID_ARG;
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is active: its blocks grow with hw_append_step; end it with hw_plan_end first");
   if (!dev) return ctx->fail(HW_ERR_WORKSPACE, "workspace is NULL");
   if ((uintptr_t)dev % kAlign) return ctx->fail(HW_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (bytes < ctx->total_bytes)
@@ -582,6 +612,10 @@ hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id) == hipSuccess && cus > 0)
       ctx->num_cus = cus;
   }
+  // The pinned staging ring of the table uploads is allocated here, at set-up, so that no
+  // append or decode allocates.
+  hw_status sst = ensure_staging(ctx);
+  if (sst != HW_OK) return sst;
   ctx->ws = dev;
   ctx->ws_bytes = bytes;
   ctx->uploaded_valid = false;
@@ -592,6 +626,7 @@ hw_status hw_append_kv(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const int32
                        const int32_t *n_tokens, const void *k, const void *v, void *stream) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is active: its blocks grow with hw_append_step; end it with hw_plan_end first");
   AppendPlan plan;
   hw_status st = plan_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
   if (st != HW_OK) return st;
@@ -632,6 +667,7 @@ hw_status hw_set_views(hw_ctx *ctx, int32_t n_workers, const int32_t *view_len,
                        const int32_t *view_blocks, const int64_t *view_offsets,
                        const int64_t *q_pos) {
   if (!ctx) return HW_ERR_INVALID_ARG;
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is active: its blocks grow with hw_append_step; end it with hw_plan_end first");
   const hw_config &g = ctx->cfg;
   if (n_workers <= 0 || n_workers > g.max_workers)
     return ctx->fail(HW_ERR_INVALID_ARG, "n_workers must be in [1, max_workers]");
@@ -681,9 +717,112 @@ hw_status hw_set_views(hw_ctx *ctx, int32_t n_workers, const int32_t *view_len,
 
 namespace {
 
-// One decode of n_new query tokens per worker (n_new = 1: the one-token step).
+// Where a decode's tables are, and how its groups are split.
+struct DecodeTables {
+  const int2 *groups = nullptr;
+  const int32_t *delta = nullptr;
+  int32_t n_groups = 0, stride = 2, splits = 1;
+  const int32_t *bounds = nullptr;      // splits + 1 cuts, or null: uniform cuts
+  const int32_t *plan_step = nullptr;   // step plans: the layer's counter of planned appends
+};
+
+// Split partials of a decode: the workspace's, or a caller-provided buffer of the same shape.
+struct Partials {
+  float *o = nullptr;
+  float *lse = nullptr;
+};
+
+Partials workspace_partials(hw_ctx *ctx) {
+  if (!ctx->ws) return Partials{};   // decode_impl rejects the call
+  return Partials{reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_o),
+                  reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_lse)};
+}
+
+// Enqueue the decode kernel of one layer and, with several partitions, the merge.
+hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
+                              float *out, float *lse, hipStream_t s, const DecodeTables &t,
+                              Partials part) {
+  const hw_config &g = ctx->cfg;
+  const int32_t n = ctx->views.n_workers;
+  const int32_t group = g.n_q_heads / g.n_kv_heads;
+  const int32_t rows = rows_total(ctx, n, n_new);
+  const size_t eb = kv_elem_bytes(ctx);
+  hw::DecodeArgs a{};
+  a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.v_layer = (char *)g.v_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.groups = t.groups;
+  a.delta = t.delta;
+  a.turn_freq = reinterpret_cast<const double *>((char *)ctx->ws + ctx->off_freq);
+  a.part_o = part.o;
+  a.part_lse = part.lse;
+  a.n_groups = t.n_groups;
+  a.n_workers = n;
+  a.n_q_heads = g.n_q_heads;
+  a.n_kv_heads = g.n_kv_heads;
+  a.group = group;
+  a.rows = rows;
+  a.n_splits = t.splits;
+  a.page_groups = g.page_size / hw::kTokGroup;
+  a.rows_per_block = hw::rows_per_block(g.kv_dtype, n_new);
+  a.inv_group = 1.0f / (float)group;
+  a.inv_rpw = 1.0f / (float)(n_new * group);
+  a.n_new = n_new;
+  a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
+  a.desc_stride = t.stride;
+  a.plan_step = t.plan_step;
+  if (t.bounds) std::copy(t.bounds, t.bounds + t.splits + 1, a.split_begin);
+  const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
+  const bool prof = ctx->prof_count < ctx->prof_capacity;
+  hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
+  hw_status st = post_launch(ctx,
+                             hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s,
+                                               prof ? ev[0] : nullptr, prof ? ev[1] : nullptr),
+                             "concurrent_decode", s);
+  if (st != HW_OK) return st;
+  if (prof) ctx->prof_count++;
+  if (t.splits > 1) {
+    hw::MergeArgs m{};
+    m.part_o = part.o;
+    m.part_lse = part.lse;
+    m.out = out;
+    m.lse = lse;
+    m.n_workers = n * n_new;   // query tokens, each merged on its own
+    m.n_q_heads = g.n_q_heads;
+    m.n_kv_heads = g.n_kv_heads;
+    m.group = group;
+    m.rows = rows;
+    m.n_splits = t.splits;
+    st = post_launch(ctx, hw::launch_merge(g.head_dim, m, s), "lse_merge", s);
+    if (st != HW_OK) return st;
+  }
+  return HW_OK;
+}
+
+// A decode under the active step plan: its tables were uploaded by hw_plan_steps.
+hw_status decode_planned(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q, float *out,
+                         float *lse, hipStream_t s, Partials part) {
+  const Plan &p = ctx->plan;
+  if (n_new != 1)
+    return ctx->fail(HW_ERR_INVALID_ARG, "several query tokens per worker are not supported under a step plan");
+  char *base = (char *)ctx->ws + ctx->off_plan;
+  DecodeTables t;
+  t.groups = reinterpret_cast<const int2 *>(base + ctx->plan_groups);
+  t.delta = reinterpret_cast<const int32_t *>(base + ctx->plan_delta);
+  t.n_groups = p.n_groups;
+  t.stride = 4;
+  t.splits = p.splits;
+  t.bounds = p.splits <= hw::kMaxBoundSplits ? p.bounds.data() : nullptr;
+  t.plan_step = reinterpret_cast<const int32_t *>(base + ctx->plan_cnt) + layer;
+  return launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
+}
+
+// One decode of n_new query tokens per worker (n_new = 1: the one-token step), with its split
+// partials in `part`.
 hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q, float *out,
-                      float *lse, hipStream_t s) {
+                      float *lse, hipStream_t s, Partials part) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   const hw_config &g = ctx->cfg;
   if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
@@ -694,7 +833,6 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
   if (!ctx->views.set) return ctx->fail(HW_ERR_STALE_VIEW, "no views set");
   const int32_t n = ctx->views.n_workers;
   char *tables = (char *)ctx->ws + ctx->off_tables;
-  const int32_t group = g.n_q_heads / g.n_kv_heads;
   const int32_t rows = rows_total(ctx, n, n_new);
   // Group descriptors: wide ones (each group's offsets beside it) for the 8-wave kernels
   // when every worker fits and each worker has one token; with several tokens, the group's
@@ -704,13 +842,24 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
                     hw::decode_waves(g.kv_dtype, rows) == 8 && rows <= hw::rows_per_block(g.kv_dtype);
   const int32_t stride = wide ? hw::kWideStride : (n_new > 1 ? 4 : 2);
 
+  if (ctx->plan.active) return decode_planned(ctx, layer, n_new, q, out, lse, s, part);
   std::vector<int64_t> sig = signature(ctx, layer);
   if (!ctx->uploaded_valid || sig != ctx->uploaded_sig || ctx->up_stride != stride) {
     Resolution r;
     hw_status st = resolve(ctx, layer, r);
     if (st != HW_OK) return st;
-    st = ensure_staging(ctx);
-    if (st != HW_OK) return st;
+    // Every check that can fail comes before the upload is staged or enqueued.
+    if (r.min_qpos < (int64_t)n_new - 1)
+      return ctx->fail(HW_ERR_STALE_VIEW, "a worker's first query token would sit below position 0");
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(s, &cap);
+    if (ce != hipSuccess) return hip_fail(ctx, ce, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+      return ctx->fail(HW_ERR_INVALID_ARG,
+                       "the views' device tables need an upload (views or lengths changed), which "
+                       "cannot be captured: decode once with these views and lengths before the "
+                       "capture, or capture steps under a step plan (hw_plan_steps)");
+    if (!ctx->staging) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
     const int32_t n_seg = (int32_t)r.seg_blocks.size();
     const int32_t n_groups = (int32_t)r.g_page.size();
     const size_t delta_bytes = align_up((size_t)n_seg * n * sizeof(int32_t));
@@ -762,32 +911,7 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
 
   const int32_t n_groups = ctx->up_n_groups;
   const int32_t splits = choose_splits(ctx, n_groups, rows, n_new);
-  const size_t eb = kv_elem_bytes(ctx);
-  hw::DecodeArgs a{};
-  a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
-  a.v_layer = (char *)g.v_pool + (size_t)layer * layer_elems(ctx) * eb;
-  a.q = q;
-  a.out = out;
-  a.lse = lse;
-  a.groups = reinterpret_cast<const int2 *>(tables + ctx->up_groups_off);
-  a.delta = reinterpret_cast<const int32_t *>(tables);
-  a.turn_freq = reinterpret_cast<const double *>((char *)ctx->ws + ctx->off_freq);
-  a.part_o = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_o);
-  a.part_lse = reinterpret_cast<float *>((char *)ctx->ws + ctx->off_part_lse);
-  a.n_groups = n_groups;
-  a.n_workers = n;
-  a.n_q_heads = g.n_q_heads;
-  a.n_kv_heads = g.n_kv_heads;
-  a.group = group;
-  a.rows = rows;
-  a.n_splits = splits;
-  a.page_groups = g.page_size / hw::kTokGroup;
-  a.rows_per_block = hw::rows_per_block(g.kv_dtype, n_new);
-  a.inv_group = 1.0f / (float)group;
-  a.inv_rpw = 1.0f / (float)(n_new * group);
-  a.n_new = n_new;
-  a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
-  a.desc_stride = ctx->up_stride;
+  const int32_t *bounds = nullptr;
   if (splits <= hw::kMaxBoundSplits) {
     const double alpha = split_alpha(ctx, rows, n_new);
     if (ctx->bounds_splits != splits || ctx->bounds_alpha != alpha) {
@@ -796,33 +920,16 @@ hw_status decode_impl(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
       ctx->bounds_splits = splits;
       ctx->bounds_alpha = alpha;
     }
-    std::copy(ctx->bounds.begin(), ctx->bounds.end(), a.split_begin);
+    bounds = ctx->bounds.data();
   }
-  const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
-  const bool prof = ctx->prof_count < ctx->prof_capacity;
-  hipEvent_t *ev = prof ? &ctx->prof_events[2 * (size_t)ctx->prof_count] : nullptr;
-  hw_status st = post_launch(ctx,
-                             hw::launch_decode(g.kv_dtype, g.head_dim, a, row_blocks, s,
-                                               prof ? ev[0] : nullptr, prof ? ev[1] : nullptr),
-                             "concurrent_decode", s);
-  if (st != HW_OK) return st;
-  if (prof) ctx->prof_count++;
-  if (splits > 1) {
-    hw::MergeArgs m{};
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.out = out;
-    m.lse = lse;
-    m.n_workers = n * n_new;   // query tokens, each merged on its own
-    m.n_q_heads = g.n_q_heads;
-    m.n_kv_heads = g.n_kv_heads;
-    m.group = group;
-    m.rows = rows;
-    m.n_splits = splits;
-    st = post_launch(ctx, hw::launch_merge(g.head_dim, m, s), "lse_merge", s);
-    if (st != HW_OK) return st;
-  }
-  return HW_OK;
+  DecodeTables t;
+  t.groups = reinterpret_cast<const int2 *>(tables + ctx->up_groups_off);
+  t.delta = reinterpret_cast<const int32_t *>(tables);
+  t.n_groups = n_groups;
+  t.stride = ctx->up_stride;
+  t.splits = splits;
+  t.bounds = bounds;
+  return launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
 }
 
 }  // namespace
@@ -831,12 +938,14 @@ extern "C" {
 
 hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float *out, float *lse,
                                void *stream) {
-  return decode_impl(ctx, layer, 1, q, out, lse, (hipStream_t)stream);
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  return decode_impl(ctx, layer, 1, q, out, lse, (hipStream_t)stream, workspace_partials(ctx));
 }
 
 hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,
                                       float *out, float *lse, void *stream) {
-  return decode_impl(ctx, layer, n_new, q, out, lse, (hipStream_t)stream);
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  return decode_impl(ctx, layer, n_new, q, out, lse, (hipStream_t)stream, workspace_partials(ctx));
 }
 
 hw_status hw_debug_kernel_events(hw_ctx *ctx, int32_t capacity) {
@@ -903,9 +1012,258 @@ hw_status hw_debug_stream_read(const void *src, size_t bytes, float *sink, int32
   return HW_OK;
 }
 
+hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const int32_t *block_ids,
+                        const int32_t *tokens_per_step, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is already active");
+  if (g.kv_dtype != HW_BF16) return ctx->fail(HW_ERR_INVALID_ARG, "step plans need bf16 pools");
+  if (!ctx->views.set) return ctx->fail(HW_ERR_STALE_VIEW, "no views set");
+  const Views &v = ctx->views;
+  if (v.has_offsets || v.has_qpos)
+    return ctx->fail(HW_ERR_INVALID_ARG, "step plans need default offsets and query positions");
+  if (n_steps < 1) return ctx->fail(HW_ERR_INVALID_ARG, "n_steps must be >= 1");
+  if (n_blocks < 0 || n_blocks > g.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "n_blocks out of range");
+  if (n_blocks > 0 && (!block_ids || !tokens_per_step))
+    return ctx->fail(HW_ERR_INVALID_ARG, "block_ids/tokens_per_step NULL");
+  std::vector<int64_t> grow(g.max_blocks, 0);
+  std::vector<char> planned(g.max_blocks, 0);
+  int64_t rows = 0;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const int32_t b = block_ids[i];
+    if (b < 0 || b >= g.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "block id out of range");
+    if (planned[b]) return ctx->fail(HW_ERR_INVALID_ARG, "block id repeated in a plan");
+    if (tokens_per_step[i] < 0) return ctx->fail(HW_ERR_INVALID_ARG, "tokens_per_step < 0");
+    planned[b] = 1;
+    grow[b] = (int64_t)n_steps * tokens_per_step[i];
+    rows += tokens_per_step[i];
+  }
+  if (rows > (1 << 20)) return ctx->fail(HW_ERR_INVALID_ARG, "too many tokens per step");
+  // Every block of the views and of the plan must have the same length in every layer: one
+  // set of tables serves all layers, each at its own count of planned appends.
+  auto equal_layers = [&](int32_t b) {
+    const auto &len = ctx->blocks[b].len;
+    return std::all_of(len.begin(), len.end(), [&](int32_t x) { return x == len[0]; });
+  };
+  for (int32_t i = 0; i < n_blocks; ++i)
+    if (!equal_layers(block_ids[i])) return ctx->fail(HW_ERR_INVALID_ARG, "a planned block's length differs between layers");
+  for (const auto &vb : v.blocks)
+    for (int32_t b : vb)
+      if (!equal_layers(b)) return ctx->fail(HW_ERR_INVALID_ARG, "a view block's length differs between layers");
+  auto len0 = [&](int32_t b) { return (int64_t)ctx->blocks[b].len[0]; };
+  auto cap = [&](int32_t b) { return len0(b) + grow[b]; };
+  for (int32_t i = 0; i < n_blocks; ++i)
+    if (cap(block_ids[i]) > g.max_position)
+      return ctx->fail(HW_ERR_INVALID_ARG, "a planned block would reach max_position");
+  const int32_t n = v.n_workers;
+  for (const auto &vb : v.blocks) {
+    int64_t total = 0;
+    for (int32_t b : vb) total += cap(b);
+    if (total > g.max_position)
+      return ctx->fail(HW_ERR_STALE_VIEW, "a view would reach max_position within the plan");
+  }
+  if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  // Pages for the whole window, taken now.
+  std::vector<int32_t> add(n_blocks, 0);
+  size_t need = 0;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const BlockState &bs = ctx->blocks[block_ids[i]];
+    const int64_t pages = (std::max<int64_t>(cap(block_ids[i]), bs.max_len()) + g.page_size - 1) / g.page_size;
+    add[i] = (int32_t)std::max<int64_t>(0, pages - (int64_t)bs.pages.size());
+    need += add[i];
+  }
+  if (need > ctx->free_stack.size())
+    return ctx->fail(HW_ERR_OUT_OF_PAGES, "not enough free pages for the plan: need " +
+                                              std::to_string(need) + ", have " +
+                                              std::to_string(ctx->free_stack.size()));
+  std::vector<std::vector<int32_t>> pages(n_blocks);
+  {
+    size_t taken = 0;
+    for (int32_t i = 0; i < n_blocks; ++i) {
+      pages[i] = ctx->blocks[block_ids[i]].pages;
+      for (int32_t k = 0; k < add[i]; ++k)
+        pages[i].push_back(ctx->free_stack[ctx->free_stack.size() - 1 - taken++]);
+    }
+  }
+  auto page_list = [&](int32_t b) -> const std::vector<int32_t> & {
+    for (int32_t i = 0; i < n_blocks; ++i)
+      if (block_ids[i] == b) return pages[i];
+    return ctx->blocks[b].pages;
+  };
+  // Segments: the blocks of the views that hold a token at the end of the plan, in order of
+  // first appearance (worker 0's view first).
+  std::vector<int32_t> seg_of(g.max_blocks, -1), seg_blocks;
+  for (const auto &vb : v.blocks)
+    for (int32_t b : vb)
+      if (cap(b) > 0 && seg_of[b] < 0) {
+        seg_of[b] = (int32_t)seg_blocks.size();
+        seg_blocks.push_back(b);
+      }
+  const int32_t n_seg = (int32_t)seg_blocks.size();
+  // Query offsets at step s: (sum of the lengths from the block to the end of the view) - 1,
+  // i.e. d0 + s * rate with rate = the tokens per step of the view's blocks from there on.
+  std::vector<int32_t> dtab((size_t)n_seg * n * 2);
+  for (size_t i = 0; i < dtab.size(); i += 2) {
+    dtab[i] = -1;
+    dtab[i + 1] = 0;
+  }
+  for (int32_t w = 0; w < n; ++w) {
+    const auto &vb = v.blocks[w];
+    int64_t suffix = 0, rate = 0;
+    for (size_t i = vb.size(); i-- > 0;) {
+      suffix += len0(vb[i]);
+      rate += grow[vb[i]] / n_steps;
+      const int32_t sg = seg_of[vb[i]];
+      if (sg >= 0) {
+        dtab[((size_t)sg * n + w) * 2] = (int32_t)(suffix - 1);
+        dtab[((size_t)sg * n + w) * 2 + 1] = (int32_t)rate;
+      }
+    }
+  }
+  // Groups at capacity: {page group of head 0, segment << 8, tokens at step 0 from the
+  // group's start (clamped to 0..32 on the device), tokens per step}.
+  const int32_t gpp = g.page_size / hw::kTokGroup;
+  std::vector<int32_t> gtab;
+  std::vector<uint8_t> seg_first;
+  for (int32_t sg = 0; sg < n_seg; ++sg) {
+    const int32_t b = seg_blocks[sg];
+    const auto &pl = page_list(b);
+    for (int64_t t = 0; t < cap(b); t += hw::kTokGroup) {
+      gtab.push_back(pl[t / g.page_size] * g.n_kv_heads * gpp + (int32_t)((t % g.page_size) / hw::kTokGroup));
+      gtab.push_back(sg << 8);
+      gtab.push_back((int32_t)(len0(b) - t));
+      gtab.push_back((int32_t)(grow[b] / n_steps));
+      seg_first.push_back(t == 0 ? 1 : 0);
+    }
+  }
+  const int32_t n_groups = (int32_t)(gtab.size() / 4);
+  const int32_t rows_q = rows_total(ctx, n);
+  const int32_t splits = choose_splits(ctx, n_groups, rows_q);
+  std::vector<int32_t> bounds;
+  if (splits <= hw::kMaxBoundSplits) {
+    bounds.resize((size_t)splits + 1);
+    partition_bounds(seg_first.data(), n_groups, splits, split_alpha(ctx, rows_q), bounds.data());
+  }
+  // Appends: {base length, tokens per step, first row, page-list offset} and the page lists.
+  std::vector<int32_t> btab, ptab;
+  int32_t row0 = 0;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    btab.push_back((int32_t)len0(block_ids[i]));
+    btab.push_back(tokens_per_step[i]);
+    btab.push_back(row0);
+    btab.push_back((int32_t)ptab.size());
+    row0 += tokens_per_step[i];
+    ptab.insert(ptab.end(), pages[i].begin(), pages[i].end());
+  }
+  // One upload of the whole region, counters zeroed; the plan is set-up, not a step, so the
+  // call waits for it.
+  const size_t region = ctx->plan_groups + gtab.size() * sizeof(int32_t);
+  std::vector<char> host(region, 0);
+  if (!btab.empty()) std::memcpy(host.data() + ctx->plan_blk, btab.data(), btab.size() * 4);
+  if (!ptab.empty()) std::memcpy(host.data() + ctx->plan_pages, ptab.data(), ptab.size() * 4);
+  if (!dtab.empty()) std::memcpy(host.data() + ctx->plan_delta, dtab.data(), dtab.size() * 4);
+  if (!gtab.empty()) std::memcpy(host.data() + ctx->plan_groups, gtab.data(), gtab.size() * 4);
+  hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus capst = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &capst);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamIsCapturing");
+  if (capst != hipStreamCaptureStatusNone)
+    return ctx->fail(HW_ERR_INVALID_ARG, "hw_plan_steps uploads tables and cannot be captured");
+  e = hipMemcpyAsync((char *)ctx->ws + ctx->off_plan, host.data(), region, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "upload of the plan's tables");
+  // Commit: the planned blocks own their pages for the whole window.
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    BlockState &bs = ctx->blocks[block_ids[i]];
+    for (int32_t k = 0; k < add[i]; ++k) {
+      bs.pages.push_back(ctx->free_stack.back());
+      ctx->free_stack.pop_back();
+    }
+  }
+  Plan &p = ctx->plan;
+  p = Plan();
+  p.active = true;
+  p.n_steps = n_steps;
+  p.blocks.assign(block_ids, block_ids + n_blocks);
+  p.tps.assign(tokens_per_step, tokens_per_step + n_blocks);
+  for (int32_t i = 0; i < n_blocks; ++i) p.base.push_back((int32_t)len0(block_ids[i]));
+  p.rows = (int32_t)rows;
+  p.n_workers = n;
+  p.n_groups = n_groups;
+  p.splits = splits;
+  p.bounds = std::move(bounds);
+  ctx->uploaded_valid = false;
+  return HW_OK;
+}
+
+hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  const Plan &p = ctx->plan;
+  if (!p.active) return ctx->fail(HW_ERR_INVALID_ARG, "no step plan is active");
+  if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (p.rows > 0 && (!k || !v)) return ctx->fail(HW_ERR_INVALID_ARG, "k/v NULL");
+  if (((uintptr_t)k | (uintptr_t)v) % 16) return ctx->fail(HW_ERR_INVALID_ARG, "k/v must be 16-byte aligned");
+  char *base = (char *)ctx->ws + ctx->off_plan;
+  const size_t eb = kv_elem_bytes(ctx);
+  hw::PlanAppendArgs a{};
+  a.k_layer = (char *)g.k_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.v_layer = (char *)g.v_pool + (size_t)layer * layer_elems(ctx) * eb;
+  a.k_src = k;
+  a.v_src = v;
+  a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
+  a.blocks = reinterpret_cast<const int32_t *>(base + ctx->plan_blk);
+  a.pages = reinterpret_cast<const int32_t *>(base + ctx->plan_pages);
+  a.step = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + layer;
+  a.overflow = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + g.n_layers;
+  a.n_blocks = (int32_t)p.blocks.size();
+  a.rows = p.rows;
+  a.n_steps = p.n_steps;
+  a.n_kv_heads = g.n_kv_heads;
+  a.page_size = g.page_size;
+  a.page_groups = g.page_size / hw::kTokGroup;
+  hipStream_t s = (hipStream_t)stream;
+  return post_launch(ctx, hw::launch_plan_append(g.kv_dtype, g.head_dim, a, s), "plan_append", s);
+}
+
+hw_status hw_plan_end(hw_ctx *ctx, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  Plan &p = ctx->plan;
+  if (!p.active) return ctx->fail(HW_ERR_INVALID_ARG, "no step plan is active");
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> cnt((size_t)g.n_layers + 1, 0);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipMemcpy(cnt.data(), (char *)ctx->ws + ctx->off_plan + ctx->plan_cnt,
+                  cnt.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(ctx, e, "read-back of the plan's step counters");
+  bool freed = false;
+  for (size_t i = 0; i < p.blocks.size(); ++i) {
+    BlockState &bs = ctx->blocks[p.blocks[i]];
+    for (int32_t l = 0; l < g.n_layers; ++l)
+      bs.len[l] = p.base[i] + std::min(cnt[l], p.n_steps) * p.tps[i];
+    const size_t keep = (size_t)((bs.max_len() + g.page_size - 1) / g.page_size);
+    while (bs.pages.size() > keep) {
+      ctx->free_stack.push_back(bs.pages.back());
+      bs.pages.pop_back();
+      freed = true;
+    }
+  }
+  if (freed) ctx->page_generation++;
+  const bool overflow = cnt[g.n_layers] != 0;
+  p = Plan();
+  ctx->uploaded_valid = false;
+  if (overflow)
+    return ctx->fail(HW_ERR_INVALID_ARG, "more planned appends than the plan's steps on some layer; "
+                                         "the extra ones were dropped");
+  return HW_OK;
+}
+
 hw_status hw_reset_block(hw_ctx *ctx, int32_t block_id) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   if (block_id < 0 || block_id >= ctx->cfg.max_blocks) return ctx->fail(HW_ERR_INVALID_ARG, "block id out of range");
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is active: its blocks grow with hw_append_step; end it with hw_plan_end first");
   BlockState &bs = ctx->blocks[block_id];
   for (auto it = bs.pages.rbegin(); it != bs.pages.rend(); ++it) ctx->free_stack.push_back(*it);
   if (!bs.pages.empty()) ctx->page_generation++;
@@ -947,6 +1305,7 @@ hw_status hw_free_pages(const hw_ctx *ctx, int32_t *n_free) {
 hw_status hw_debug_reserve(hw_ctx *ctx, int32_t layer, int32_t n_blocks, const int32_t *block_ids,
                            const int32_t *n_tokens, int32_t *runs, int32_t cap, int32_t *n_runs) {
   if (!ctx) return HW_ERR_INVALID_ARG;
+  if (ctx->plan.active) return ctx->fail(HW_ERR_INVALID_ARG, "a step plan is active: its blocks grow with hw_append_step; end it with hw_plan_end first");
   AppendPlan plan;
   hw_status st = plan_append(ctx, layer, n_blocks, block_ids, n_tokens, plan);
   if (st != HW_OK) return st;
@@ -986,7 +1345,8 @@ hw_status hw_debug_resolve(hw_ctx *ctx, int32_t layer, int32_t *segs, int32_t *d
   const int32_t ns = (int32_t)r.seg_blocks.size(), ng = (int32_t)r.g_page.size();
   if (n_segs) *n_segs = ns;
   if (n_groups) *n_groups = ng;
-  if (n_splits) *n_splits = choose_splits(ctx, ng, rows_total(ctx, r.n_workers));
+  if (n_splits)
+    *n_splits = ctx->plan.active ? ctx->plan.splits : choose_splits(ctx, ng, rows_total(ctx, r.n_workers));
   if (ns > cap_segs || ng > cap_groups) return ctx->fail(HW_ERR_INVALID_ARG, "buffers too small");
   if (segs) std::copy(r.seg_blocks.begin(), r.seg_blocks.end(), segs);
   if (delta) std::copy(r.delta.begin(), r.delta.end(), delta);

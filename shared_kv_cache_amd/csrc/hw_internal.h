@@ -89,10 +89,35 @@ struct DecodeArgs {
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];
   int32_t desc_stride;     // ints per group descriptor: 2, 4, or kWideStride (8-wave kernels only)
+  // Step plan: the layer's counter of planned appends (null: no plan). Descriptors are then
+  // {x, segment << 8, v0, rate} and delta holds {d0, rate} pairs (see the kernel).
+  const int32_t *plan_step;
 };
 
 
 hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStream_t s);
+
+// The append of one planned step of one layer (a step plan, hw_plan_steps): every planned
+// block b takes its tokens_per_step tokens at local positions base(b) + s * tps(b) + j, s
+// being the layer's counter of planned appends, which the kernel then advances.
+struct PlanAppendArgs {
+  void *k_layer;
+  void *v_layer;
+  const void *k_src;       // [rows][n_kv_heads][head_dim], rows in planned-block order
+  const void *v_src;
+  const float2 *trig;      // [max_position][head_dim/2] (cos, sin)
+  const int32_t *blocks;   // [n_blocks][4] {base length, tokens per step, first row, page-list offset}
+  const int32_t *pages;    // page lists of the planned blocks (capacity of the whole plan)
+  int32_t *step;           // the layer's counter of planned appends
+  int32_t *overflow;       // set to 1 by an append past the plan's last step (dropped)
+  int32_t n_blocks;
+  int32_t rows;            // tokens per step, all planned blocks
+  int32_t n_steps;
+  int32_t n_kv_heads;
+  int32_t page_size;
+  int32_t page_groups;
+};
+hipError_t launch_plan_append(hw_dtype dt, int head_dim, const PlanAppendArgs &a, hipStream_t s);
 struct MergeArgs {
   const float *part_o;
   const float *part_lse;

@@ -17,7 +17,9 @@
 // the row index in the MFMA N dimension, so one lane owns one row in S, P and O and the
 // softmax needs only two cross-lane exchanges per 32 tokens. The pool layouts (hogwild.h)
 // put each lane's 16-byte operand at lane * 16 of a 1 KiB run, so every load is coalesced
-// and lands in operand layout with no LDS staging.
+// and lands in operand layout with no shuffle: straight into registers, or (the 8-wave bf16
+// kernels with wide descriptors) through a per-wave LDS stage that LDS-DMA loads fill while
+// the wave computes the previous group.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -147,6 +149,106 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// plan_append: the append of one planned step of one layer, in ONE workgroup. Every thread
+// reads the layer's step counter s first; after a barrier, thread 0 advances it, so no
+// thread can see the advanced value. One item = (row, KV head, 8-dim chunk): the key's 8
+// rotated pairs (dims c, c + D/2 for c in the chunk) and the same 16 dims of the value.
+// ------------------------------------------------------------------------------------
+template <typename KV, int D>
+__global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
+  const int s = a.step[0];
+  if (s >= a.n_steps) {   // past the plan: nothing is written, the host reports it
+    if (threadIdx.x == 0) a.overflow[0] = 1;
+    return;
+  }
+  constexpr int kChunks = D / 16;
+  constexpr int kVec = 16 / (int)sizeof(KV);   // elements per 16-byte access
+  static_assert(8 % kVec == 0, "8-element chunks in 16-byte accesses");
+  const int hkv = a.n_kv_heads;
+  const KV *__restrict__ ksrc = static_cast<const KV *>(a.k_src);
+  const KV *__restrict__ vsrc = static_cast<const KV *>(a.v_src);
+  KV *__restrict__ kdst = static_cast<KV *>(a.k_layer);
+  KV *__restrict__ vdst = static_cast<KV *>(a.v_layer);
+  const int items = a.rows * hkv * kChunks;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int c8 = it % kChunks;
+    const int h = (it / kChunks) % hkv;
+    const int r = it / (kChunks * hkv);
+    int bi = 0;
+    for (int i = 0; i < a.n_blocks; ++i) {
+      const int r0 = a.blocks[4 * i + 2];
+      if (r >= r0 && r < r0 + a.blocks[4 * i + 1]) bi = i;
+    }
+    const int pos = a.blocks[4 * bi] + s * a.blocks[4 * bi + 1] + (r - a.blocks[4 * bi + 2]);
+    const int page = a.pages[a.blocks[4 * bi + 3] + pos / a.page_size];
+    const int t = pos % a.page_size;
+    const size_t grp = ((size_t)page * hkv + h) * a.page_groups + t / 32;
+    const int u = t & 31;
+    const size_t src = ((size_t)r * hkv + h) * D;
+    // Every load first, 16 bytes at a time: the 8 dims of the chunk in each half of the
+    // head, for K and V, and the chunk's 8 (cos, sin) pairs.
+    uint4 kl[8 / kVec], kh[8 / kVec], vl[8 / kVec], vh[8 / kVec];
+    float4 cs[4];
+#pragma unroll
+    for (int j = 0; j < 8 / kVec; ++j) {
+      kl[j] = *reinterpret_cast<const uint4 *>(ksrc + src + 8 * c8 + kVec * j);
+      kh[j] = *reinterpret_cast<const uint4 *>(ksrc + src + D / 2 + 8 * c8 + kVec * j);
+      vl[j] = *reinterpret_cast<const uint4 *>(vsrc + src + 8 * c8 + kVec * j);
+      vh[j] = *reinterpret_cast<const uint4 *>(vsrc + src + D / 2 + 8 * c8 + kVec * j);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      cs[j] = reinterpret_cast<const float4 *>(a.trig + (size_t)pos * (D / 2) + 8 * c8)[j];
+    const KV *x0 = reinterpret_cast<const KV *>(kl), *x1 = reinterpret_cast<const KV *>(kh);
+    const KV *w0 = reinterpret_cast<const KV *>(vl), *w1 = reinterpret_cast<const KV *>(vh);
+    const float *cf = reinterpret_cast<const float *>(cs);
+    float lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a0, a1;
+      if constexpr (sizeof(KV) == 2) {
+        a0 = __uint_as_float((uint32_t)(*(const uint16_t *)&x0[e]) << 16);
+        a1 = __uint_as_float((uint32_t)(*(const uint16_t *)&x1[e]) << 16);
+      } else {
+        a0 = x0[e];
+        a1 = x1[e];
+      }
+      rotate_pair(a0, a1, cf[2 * e], cf[2 * e + 1], lo[e], hi[e]);
+    }
+    // Keys: the chunk's 8 dims of one token are contiguous in the K layout (16 or 32 bytes).
+    KV *kg = kdst + grp * (size_t)(32 * D);
+    KV *klo = kg + k_index(u, 8 * c8), *khi = kg + k_index(u, D / 2 + 8 * c8);
+    if constexpr (sizeof(KV) == 2) {
+      uint4 wlo, whi;
+      wlo.x = bf16_rne_bits(lo[0]) | ((uint32_t)bf16_rne_bits(lo[1]) << 16);
+      wlo.y = bf16_rne_bits(lo[2]) | ((uint32_t)bf16_rne_bits(lo[3]) << 16);
+      wlo.z = bf16_rne_bits(lo[4]) | ((uint32_t)bf16_rne_bits(lo[5]) << 16);
+      wlo.w = bf16_rne_bits(lo[6]) | ((uint32_t)bf16_rne_bits(lo[7]) << 16);
+      whi.x = bf16_rne_bits(hi[0]) | ((uint32_t)bf16_rne_bits(hi[1]) << 16);
+      whi.y = bf16_rne_bits(hi[2]) | ((uint32_t)bf16_rne_bits(hi[3]) << 16);
+      whi.z = bf16_rne_bits(hi[4]) | ((uint32_t)bf16_rne_bits(hi[5]) << 16);
+      whi.w = bf16_rne_bits(hi[6]) | ((uint32_t)bf16_rne_bits(hi[7]) << 16);
+      *reinterpret_cast<uint4 *>(klo) = wlo;
+      *reinterpret_cast<uint4 *>(khi) = whi;
+    } else {
+      reinterpret_cast<float4 *>(klo)[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+      reinterpret_cast<float4 *>(klo)[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+      reinterpret_cast<float4 *>(khi)[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+      reinterpret_cast<float4 *>(khi)[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
+    }
+    // Values: one element per dim (the V layout keeps 8 tokens of a dim together).
+    KV *vg = vdst + grp * (size_t)(32 * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vg[v_index(u, 8 * c8 + e)] = w0[e];
+      vg[v_index(u, D / 2 + 8 * c8 + e)] = w1[e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.step[0] = s + 1;
+}
+
+// ------------------------------------------------------------------------------------
 // concurrent_decode
 // ------------------------------------------------------------------------------------
 
@@ -222,6 +324,23 @@ struct Frag<__bf16, D> {
     return r;
   }
   static __device__ __forceinline__ POp make_p(const float *p) { return make_q(p); }
+  // Zero the values of the group's slots u >= nvalid, which no token occupies: their pool
+  // bytes are whatever the memory held, and a probability of 0 times a NaN is still NaN.
+  // Lane l holds tokens 8 * (l / 16) + e, e = 0..7, two per dword.
+  __device__ __forceinline__ void mask_tail(int nvalid, int lane) {
+    const int u0 = 8 * (lane >> 4);
+    uint32_t m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      m[j] = (u0 + 2 * j < nvalid ? 0x0000FFFFu : 0u) | (u0 + 2 * j + 1 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      v[dt].x &= m[0];
+      v[dt].y &= m[1];
+      v[dt].z &= m[2];
+      v[dt].w &= m[3];
+    }
+  }
   __device__ __forceinline__ f32x4 score(int c, int hh, const QOp &q, f32x4 acc) const {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[c][hh]), q, acc,
                                                    0, 0, 0);
@@ -275,6 +394,14 @@ struct Frag<float, D> {
     return r;
   }
   static __device__ __forceinline__ POp make_p(const float *p) { return make_q(p); }
+  // As for bf16: lane l holds tokens 8 * (l / 16) + e of one dim in v[dt].x[e].
+  __device__ __forceinline__ void mask_tail(int nvalid, int lane) {
+    const int u0 = 8 * (lane >> 4);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[dt].x[e] = u0 + e < nvalid ? v[dt].x[e] : 0.0f;
+  }
   // K step e of chunk c covers dims 32c + 8g + e for lane group g on both operands.
   __device__ __forceinline__ f32x4 score(int c, int hh, const QOp &q, f32x4 acc) const {
 #pragma unroll
@@ -320,13 +447,20 @@ typedef __attribute__((address_space(4))) const int ConstInt;
 struct GDesc {
   int x = 0, y = 0, ls = 0;
 };
-template <bool MT>
-__device__ __forceinline__ GDesc load_desc(const int2 *groups, long long i, int stride) {
+// Under a step plan (PLAN) a descriptor is {x, segment << 8, v0, rate}: the group holds
+// clamp(v0 + pstep * rate, 0, 32) tokens after pstep planned appends of the layer.
+template <bool MT, bool PLAN = false>
+__device__ __forceinline__ GDesc load_desc(const int2 *groups, long long i, int stride,
+                                           int pstep = 0) {
   const ConstInt *p = (const ConstInt *)groups + (long long)stride * i;
   GDesc d;
   d.x = p[0];
   d.y = p[1];
   if constexpr (MT) d.ls = p[2];
+  if constexpr (PLAN) {
+    const int v = p[2] + pstep * p[3];
+    d.y = (d.y & ~255) | (v < 0 ? 0 : (v > 32 ? 32 : v));
+  }
   return d;
 }
 
@@ -381,12 +515,25 @@ __device__ __forceinline__ void fetch_group(Stage<KV, D> &st, GDesc desc, const 
   st.f.template load<true>(kl + gb, vl + gb, lane);
 }
 
+// The query offset of worker w for the block of segment seg. Under a step plan the table
+// holds {d0, rate} pairs and the offset is d0 + pstep * rate ({-1, 0}: not visible).
+template <bool PLAN>
+__device__ __forceinline__ int delta_at(const DecodeArgs &a, int seg, int w, int pstep) {
+  const size_t i = (size_t)seg * a.n_workers + w;
+  if constexpr (PLAN) {
+    const int2 e = reinterpret_cast<const int2 *>(a.delta)[i];
+    return e.x + pstep * e.y;
+  } else {
+    return a.delta[i];
+  }
+}
+
 // Issue the loads of the query offsets of the lane's rows for the block of segment seg.
-template <int RT>
+template <bool PLAN, int RT>
 __device__ __forceinline__ void fetch_delta(int (&dl)[RT], int seg, const DecodeArgs &a,
-                                            const int *row_w) {
+                                            const int *row_w, int pstep) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) dl[rt] = a.delta[(size_t)seg * a.n_workers + row_w[rt]];
+  for (int rt = 0; rt < RT; ++rt) dl[rt] = delta_at<PLAN>(a, seg, row_w[rt], pstep);
 }
 
 __device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -427,11 +574,17 @@ constexpr int phase_segments() {
 //
 // MT (several query tokens per worker, 4-int descriptors): rows are (worker, token, head) and
 // each row's keys after its token are masked. One-token kernels carry none of that state.
-template <typename KV, int D, int RT, int NW, int NST, bool WIDE, bool MT>
+//
+// PLAN (a step plan, one token per worker, narrow 4-int descriptors): group sizes and query
+// offsets are affine in the number of planned appends of the layer, read from the device
+// at launch (see load_desc and delta_at), so the launch needs no host-side tables update
+// from step to step.
+template <typename KV, int D, int RT, int NW, int NST, bool WIDE, bool MT, bool PLAN>
 __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
   static_assert(NST == 1 || NST == 2, "one or two stages");
   static_assert(!WIDE || NST == 1, "wide descriptors: single-stage kernels");
   static_assert(!(WIDE && MT), "wide descriptors: one token per worker");
+  static_assert(!(PLAN && (WIDE || MT)), "step plans: narrow descriptors, one token");
   constexpr bool COOP = NST == 2;
   using F = Frag<KV, D>;
   using S = Stage<KV, D>;
@@ -533,10 +686,13 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // still issues its loads, from descriptor (0, 0): page 0 of the head and the first row of
   // the offset table, both always allocated; the data goes unused. Loads issued
   // unconditionally keep the waits for each stage exact.
+  // Step plan: planned appends of this layer so far (wave-uniform, scalar cache).
+  int pstep = 0;
+  if constexpr (PLAN) pstep = *(const ConstInt *)a.plan_step;
   int s_lo = 0, s_hi = -1;
   if (COOP && end > begin) {
     s_lo = load_desc<MT>(a.groups, begin, a.desc_stride).y >> 8;
-    s_hi = load_desc<MT>(a.groups, end - 1, a.desc_stride).y >> 8;
+    s_hi = load_desc<MT>(a.groups, end - 1, a.desc_stride).y >> 8;   // (segments: no plan term)
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   GDesc desc, next, next2;
@@ -544,7 +700,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   WideOff ow, ow_next, ow_next2;
   auto desc_at = [&](long long i, WideOff &off) __attribute__((always_inline)) {
     if constexpr (WIDE) return load_desc_wide(a.groups, i, off);
-    else return load_desc<MT>(a.groups, i, a.desc_stride);
+    else return load_desc<MT, PLAN>(a.groups, i, a.desc_stride, pstep);
   };
   if (wcount > 0) desc = desc_at(wfirst, ow);   // only groups of this wave's run
   if (wcount > 1) next = desc_at(wfirst + 1, ow_next);
@@ -576,7 +732,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
 #pragma unroll
     for (int k = 0; k < DLPT; ++k) {
       const int t = tid + k * NT;
-      dlv[k] = t < cnt ? a.delta[(size_t)(seg_lo + t / nw) * a.n_workers + wlo + t % nw] : -1;
+      dlv[k] = t < cnt ? delta_at<PLAN>(a, seg_lo + t / nw, wlo + t % nw, pstep) : -1;
     }
   };
   auto store_offsets = [&]() __attribute__((always_inline)) {
@@ -593,9 +749,9 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     fetch_group(st, desc, kl, vl, head_groups, lane);
     wide_rows(dl_cur, ow);
   } else {
-    fetch_delta(dl_cur, desc.y >> 8, a, row_w);
+    fetch_delta<PLAN>(dl_cur, desc.y >> 8, a, row_w, pstep);
     fetch_group(st, desc, kl, vl, head_groups, lane);
-    fetch_delta(dl_next, next.y >> 8, a, row_w);
+    fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
   }
   if (wcount > 2) next2 = desc_at(wfirst + 2, ow_next2);
   // Stage the queries, pre-scaled by softmax_scale * log2(e), the offsets and the rotation
@@ -672,7 +828,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // One group: visibility and (NST = 1, new segment) rotation, scores, online softmax, PV.
   // seg_lo: first segment of the current phase (COOP); delta: the lane's rows' offsets for
   // the group's block (NST = 1).
-  auto process = [&](const S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
+  auto process = [&](S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
     const int seg = sg.desc_y >> 8;
     const int nvalid = sg.desc_y & 255;
     const QOp *qs;
@@ -752,6 +908,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         any_mask |= __builtin_amdgcn_ballot_w64(rowvis[rt] && ls + nvalid - 1 > rowoff[rt]) != 0;
     }
     if (any_mask) {
+      if (nvalid < 32) sg.f.mask_tail(nvalid, lane);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -860,7 +1017,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         } else {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) dl_cur[rt] = dl_next[rt];
-          fetch_delta(dl_next, next.y >> 8, a, row_w);
+          fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
         }
         next2 = desc_at(min(wfirst + i + 2, wlast), ow_next2);
       }
@@ -888,7 +1045,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         process(st, seg_lo, dl_cur);
         desc = next;
         next = next2;
-        next2 = load_desc<MT>(a.groups, min(wfirst + i + 3, wlast), a.desc_stride);
+        next2 = load_desc<MT, PLAN>(a.groups, min(wfirst + i + 3, wlast), a.desc_stride, pstep);
         ++i;
       }
     }
@@ -1049,6 +1206,22 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_plan_append(hw_dtype dt, int head_dim, const PlanAppendArgs &a, hipStream_t s) {
+  dim3 grid(1), block(1024);
+  if (dt == HW_BF16) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((plan_append_kernel<__bf16, 128>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((plan_append_kernel<__bf16, 64>), grid, block, 0, s, a);
+  } else {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((plan_append_kernel<float, 128>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((plan_append_kernel<float, 64>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 // Launched with hipExtLaunchKernelGGL so that optional start/stop events are recorded by
 // the kernel's own dispatch (null events: a plain launch). bf16 pools: up to 32 rows per
 // workgroup run on 8 single-stage waves; 33..64 rows on 4 two-stage waves.
@@ -1057,13 +1230,22 @@ static hipError_t launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hip
                                      hipEvent_t e0, hipEvent_t e1) {
   const dim3 b8(8 * 64), b4(4 * 64);
   const bool wide = !MT && a.desc_stride == kWideStride;
-  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
-  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+  if constexpr (!MT) {
+    if (a.plan_step) {   // a step plan: narrow descriptors, affine in the layer's step count
+      if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, false, true>), grid, b8, 0, s, e0, e1, 0, a);
+      else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, false, true>), grid, b8, 0, s, e0, e1, 0, a);
+      else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false, false, true>), grid, b4, 0, s, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false, false, true>), grid, b4, 0, s, e0, e1, 0, a);
+      return hipSuccess;
+    }
+  }
+  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
   else if constexpr (MT) return hipErrorInvalidValue;   // several tokens: blocks of <= 32 rows
-  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false, MT>), grid, b4, 0, s, e0, e1, 0, a);
+  else if (rt == 3) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 3, 4, 2, false, MT, false>), grid, b4, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 4, 4, 2, false, MT, false>), grid, b4, 0, s, e0, e1, 0, a);
   return hipSuccess;
 }
 
@@ -1071,9 +1253,9 @@ template <int D, bool MT>
 static void launch_decode_f32(const DecodeArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 b8(8 * 64);
   if (!MT && a.desc_stride == kWideStride)
-    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, !MT, MT>), grid, b8, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
   else
-    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, false, MT>), grid, b8, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((concurrent_decode_kernel<float, D, 1, 8, 1, false, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
 }
 
 // Several query tokens per worker (n_new > 1) run the MT kernels; wide descriptors are only

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 # every symbol the headers declare
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_concurrent_decode_tokens",
-           "hw_reset_block",
+           "hw_reset_block", "hw_plan_steps", "hw_append_step", "hw_plan_end",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
            "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
            "hw_debug_stream_read", "hw_debug_partition"]
@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_concurrent_decode_tokens": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                                 c_void_p, c_void_p]),
         "hw_reset_block": (c_int, [c_void_p, c_int32]),
+        "hw_plan_steps": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_void_p]),
+        "hw_append_step": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+        "hw_plan_end": (c_int, [c_void_p, c_void_p]),
         "hw_set_split": (c_int, [c_void_p, c_int32]),
         "hw_block_info": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_int32, P32]),
         "hw_free_pages": (c_int, [c_void_p, P32]),
@@ -168,6 +171,21 @@ def hw_concurrent_decode_tokens(ctx, layer: int, n_new: int, q_ptr: int, out_ptr
 
 def hw_reset_block(ctx, block_id: int) -> None:
     _check(ctx, load_library().hw_reset_block(ctx, block_id))
+
+
+def hw_plan_steps(ctx, n_steps: int, block_ids: Sequence[int], tokens_per_step: Sequence[int],
+                  stream: int) -> None:
+    _check(ctx, load_library().hw_plan_steps(ctx, n_steps, len(block_ids), _i32(block_ids),
+                                             _i32(tokens_per_step), c_void_p(stream)))
+
+
+def hw_append_step(ctx, layer: int, k_ptr: int, v_ptr: int, stream: int) -> None:
+    _check(ctx, load_library().hw_append_step(ctx, layer, c_void_p(k_ptr), c_void_p(v_ptr),
+                                              c_void_p(stream)))
+
+
+def hw_plan_end(ctx, stream: int) -> None:
+    _check(ctx, load_library().hw_plan_end(ctx, c_void_p(stream)))
 
 
 def hw_set_split(ctx, n_splits: int) -> None:
@@ -337,6 +355,23 @@ class HogwildCache:
         hw_concurrent_decode_tokens(self.ctx, layer, n_new, q.data_ptr(), out.data_ptr(),
                                     lse.data_ptr() if lse is not None else None, self._stream())
         return out, lse
+
+    def plan_steps(self, n_steps: int, block_ids: Sequence[int], tokens_per_step: Sequence[int]) -> None:
+        hw_plan_steps(self.ctx, n_steps, block_ids, tokens_per_step, self._stream())
+        self.plan_rows = int(sum(tokens_per_step))
+
+    def append_step(self, layer: int, k, v) -> None:
+        """One planned step's tokens of one layer: k, v [rows, n_kv_heads, head_dim]."""
+        shape = (self.plan_rows, self.n_kv_heads, self.head_dim)
+        for t in (k, v):
+            if t.dtype != self.kv_torch_dtype or tuple(t.shape) != shape or not t.is_contiguous() \
+                    or t.device != self.device:
+                raise HwError(HW_ERR_INVALID_ARG, f"k/v must be contiguous {self.kv_torch_dtype} "
+                                                  f"{shape} on {self.device}")
+        hw_append_step(self.ctx, layer, k.data_ptr(), v.data_ptr(), self._stream())
+
+    def plan_end(self) -> None:
+        hw_plan_end(self.ctx, self._stream())
 
     def block_info(self, block: int, layer: int = 0):
         return hw_block_info(self.ctx, block, layer)

@@ -60,6 +60,30 @@ def max_row_rel(got, ref) -> float:
     return float(np.max(num / den))
 
 
+# Parity bar of the GPU path against the oracle: relative L2 over the whole output, and the
+# same bound on every (worker, [token,] head) row; lse in absolute terms (natural log).
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def assert_parity(name, out, lse, ref, ref_lse, tol, say=print):
+    """out/ref [..., D], lse/ref_lse [...]. Rows whose reference lse is -inf (no key) must be
+    exactly 0 with lse -inf; every other row is held to tol, in rel L2 and in lse."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    lse = np.asarray(lse, np.float64)
+    ref_lse = np.asarray(ref_lse, np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.all(np.isneginf(lse[~fin])) and np.all(out[~fin] == 0.0), f"{name}: empty rows"
+    err = rel_l2(out[fin], ref[fin])
+    row = max_row_rel(out[fin], ref[fin])
+    lse_err = float(np.max(np.abs(lse[fin] - ref_lse[fin])))
+    say(f"{name}: rel_l2 {err:.3e} max_row {row:.3e} lse_abs {lse_err:.3e} (tol {tol:g})")
+    assert err <= tol, f"{name}: rel_l2 {err}"
+    assert row <= tol, f"{name}: max_row {row}"
+    assert lse_err <= tol, f"{name}: lse {lse_err}"
+    return err, row, lse_err
+
+
 def decode_np(cache: H.HogwildCache, layer: int, q: np.ndarray):
     qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(DEV)
     out, lse = cache.decode(layer, qt)

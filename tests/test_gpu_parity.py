@@ -1,8 +1,10 @@
 """Parity of the gfx950 path against the fp64 oracle, through the C ABI.
 
-Tolerances: relative L2 over all (worker, head, dim) of a layer <= 1e-5 for the
-fp32 configuration and <= 1e-2 for bf16 K/V; the stored pool bytes are
-bit-exact (V copied, K = the oracle's stored-key reference).
+Tolerances (hw_testlib.assert_parity): relative L2 over all (worker, head, dim)
+of a layer <= 1e-5 for the fp32 configuration and <= 1e-2 for bf16 K/V, the
+same bound on every single (worker, head) row, and |lse - lse_ref| <= the same
+number in absolute terms; the stored pool bytes are bit-exact (V copied, K =
+the oracle's stored-key reference).
 """
 
 import math
@@ -15,12 +17,17 @@ from oracle import hogwild_oracle as O
 from shared_kv_cache_amd import hogwild as H
 from shared_kv_cache_amd import workloads as W
 
-from hw_testlib import (DEV, decode_np, fill_layer, k_pool_token, kv_tensor, make_cache, max_row_rel,
-                        oracle_blocks, rel_l2, v_pool_token, variant_workload)
+from hw_testlib import (DEV, TOL, assert_parity, decode_np, fill_layer, k_pool_token, kv_tensor,
+                        make_cache, oracle_blocks, rel_l2, v_pool_token, variant_workload)
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 1e-2}
+# Agreement of one decode under different partition counts (bf16 pools). Each partition
+# rounds its probabilities to bf16 against its own running maximum, so two partition
+# counts round different numbers: relative 2^-9 per probability, independent across keys,
+# which averages to about 2e-3 over a layer (measured 2.2e-3 on w2_4k between 1 and 256
+# partitions). Twice that is the bound; fp32 pools agree to 1e-6.
+SPLIT_TOL_BF16 = 5e-3
 
 
 def _say(*a):
@@ -34,13 +41,9 @@ def _check_layer(cache, wl, layer, heads=None, tol=None, offsets=None, q_pos=Non
     ref, ref_lse = O.concurrent_attention(q.astype(np.float64), oracle_blocks(wl, layer), views,
                                           offsets=offsets, q_pos=q_pos, theta=wl.theta, heads=heads)
     hs = list(range(wl.n_q_heads)) if heads is None else list(heads)
-    err = rel_l2(out[:, hs], ref[:, hs])
-    lse_err = float(np.max(np.abs(lse[:, hs] - ref_lse[:, hs])))
-    _say(f"{wl.name} layer {layer}: rel_l2 {err:.3e} max_row {max_row_rel(out[:, hs], ref[:, hs]):.3e} "
-         f"lse_abs {lse_err:.3e}")
     tol = TOL[wl.kv_dtype] if tol is None else tol
-    assert err <= tol
-    assert lse_err <= max(tol, 1e-6) * 10
+    assert_parity(f"{wl.name} layer {layer}", out[:, hs], lse[:, hs], ref[:, hs], ref_lse[:, hs],
+                  tol, _say)
     return out, lse
 
 
@@ -117,9 +120,7 @@ def test_w2_4k_parity_and_split_invariance():
     o256, l256 = decode_np(cache, 1, q)
     H.hw_set_split(cache.ctx, 0)
     _say(f"split 1 vs 256: {rel_l2(o256, o1):.3e}")
-    # Each partition rounds its probabilities to bf16 against its own running max, so
-    # split counts differ at the bf16 level (the fp32 pool case above agrees to 1e-6).
-    assert rel_l2(o256, o1) <= TOL["bf16"]
+    assert rel_l2(o256, o1) <= SPLIT_TOL_BF16
     assert np.max(np.abs(l256 - l1)) <= 1e-4
     cache.close()
 
@@ -178,9 +179,7 @@ def test_many_rows_multiple_row_blocks_and_empty_view():
     assert np.all(out[4] == 0.0) and np.all(np.isneginf(lse[4]))
     blocks = {b: tuple(np.asarray(x, np.float64) for x in wl.kv(0, b)) for b in range(6)}
     ref, ref_lse = O.concurrent_attention(q[:4].astype(np.float64), blocks, views[:4], theta=wl.theta)
-    err = rel_l2(out[:4], ref)
-    _say(f"rows80: rel_l2 {err:.3e}")
-    assert err <= 1e-2
+    assert_parity("rows80", out[:4], lse[:4], ref, ref_lse, TOL["bf16"], _say)
     cache.close()
 
 
@@ -204,10 +203,7 @@ def test_every_bf16_kernel_variant(head_dim, n_workers, group):
     for splits in (0, 1, 3, 40, 80):
         H.hw_set_split(cache.ctx, splits)
         out, lse = decode_np(cache, 0, q)
-        err = rel_l2(out, ref)
-        _say(f"{wl.name} splits {splits}: rel_l2 {err:.3e}")
-        assert err <= TOL["bf16"]
-        assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+        assert_parity(f"{wl.name} splits {splits}", out, lse, ref, ref_lse, TOL["bf16"], _say)
     cache.close()
 
 
@@ -250,10 +246,8 @@ def test_cache_layouts_as_views(n_workers, n_q_heads):
         for splits in (0, 1, 7):
             H.hw_set_split(cache.ctx, splits)
             out, lse = decode_np(cache, 0, q)
-            err = rel_l2(out, ref)
-            _say(f"{wl.name} {layout} splits {splits}: rel_l2 {err:.3e}")
-            assert err <= TOL["bf16"]
-            assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+            assert_parity(f"{wl.name} {layout} splits {splits}", out, lse, ref, ref_lse,
+                          TOL["bf16"], _say)
     cache.close()
 
 
@@ -293,10 +287,8 @@ def test_step_commit_flow_with_block_reuse():
         q = wl.q(0, step)
         ref, ref_lse = O.concurrent_attention(q.astype(np.float64), blocks, views, theta=wl.theta)
         out, lse = decode_np(cache, 0, q)
-        err = rel_l2(out, ref)
-        _say(f"commit flow step {step}: history {len(hist)} blocks, rel_l2 {err:.3e}")
-        assert err <= TOL["bf16"]
-        assert np.max(np.abs(lse - ref_lse)) <= TOL["bf16"] * 10
+        assert_parity(f"commit flow step {step} ({len(hist)} history blocks)", out, lse, ref,
+                      ref_lse, TOL["bf16"], _say)
     cache.close()
 
 
@@ -373,6 +365,65 @@ def test_errors_leave_gpu_state_unchanged():
     cache.close()
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "variant"])
+def test_pools_holding_nan_bits(name):
+    # Pools that were never initialised may hold any bits. Fill both with NaN patterns
+    # before the appends: the unoccupied slots of every block's last group then hold NaN,
+    # and the decode must still match the oracle (masked scores, zeroed values).
+    wl = W.make("tiny_fp32") if name == "tiny_fp32" else variant_workload(128, 4, 8)
+    cache = make_cache(wl, max_splits=64)
+    for pool in (cache.k_pool, cache.v_pool):
+        (pool.view(torch.int16) if pool.dtype == torch.bfloat16 else pool.view(torch.int32)).fill_(-1)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    q = wl.q(0)
+    ref, ref_lse = O.concurrent_attention(q.astype(np.float64), oracle_blocks(wl, 0), wl.views(),
+                                          theta=wl.theta)
+    for splits in (0, 1, 5):
+        H.hw_set_split(cache.ctx, splits)
+        out, lse = decode_np(cache, 0, q)
+        assert np.all(np.isfinite(out))
+        assert_parity(f"{wl.name} NaN pools splits {splits}", out, lse, ref, ref_lse,
+                      TOL[wl.kv_dtype], _say)
+    cache.close()
+
+
+def test_capture_refuses_a_table_upload():
+    # A decode whose views' tables must be uploaded (views or lengths changed) cannot sit in
+    # a stream capture: it returns an error and enqueues nothing; the same decode after an
+    # eager one (tables current) captures and replays to the eager result.
+    wl = _layout_workload(4, 40, seed=37)
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    q = torch.from_numpy(wl.q(0)).to(DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], device=DEV)
+    cache.set_views(wl.views("stepwise"))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with pytest.raises(H.HwError) as e:
+        with torch.cuda.graph(g, stream=side):
+            cache.decode(0, q, out=out, lse=lse)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    assert "capture" in e.value.message
+    torch.cuda.synchronize()
+    cache.decode(0, q, out=out, lse=lse)               # eager: uploads the tables
+    torch.cuda.synchronize()
+    eager = out.clone(), lse.clone()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=side):
+        cache.decode(0, q, out=out, lse=lse)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1])
+    cache.close()
+
+
 # ------------------------------------------------------- full-size configs
 
 def test_w4_16k_parity_sampled_layers():
@@ -416,21 +467,45 @@ def test_w8_32k_parity_across_steps():
             q = wl.q(layer, step)
             out, lse = decode_np(cache, layer, q)
             ref, ref_lse = O.concurrent_attention(q.astype(np.float64), blocks, wl.views(), theta=wl.theta)
-            err = rel_l2(out, ref)
-            _say(f"w8_32k step {step} layer {layer}: rel_l2 {err:.3e}")
-            assert err <= 1e-2
+            assert_parity(f"w8_32k step {step} layer {layer}", out, lse, ref, ref_lse,
+                          TOL["bf16"], _say)
+    cache.close()
+
+
+def _sink_heads(wl, salt):
+    """Four query heads of the 131k-token case: three seeded heads outside the sink group and
+    one inside it (KV head 7 holds the four keys scaled x8, query heads 35..39)."""
+    rng = np.random.default_rng(wl.seed + salt)
+    return sorted(set(int(x) for x in rng.choice(35, size=3, replace=False)) |
+                  {int(rng.integers(35, 40))})
+
+
+def test_w4_128k_sinks_automatic_splits_two_layer_pools():
+    # The launch configuration the bench times: the automatic partition count with
+    # host-chosen bounds (the bounded-partition path), on two of the four layer pools.
+    wl = W.make("w4_128k_sinks", n_layers=2)
+    cache = make_cache(wl)
+    for layer in range(2):
+        fill_layer(cache, wl, layer)
+    cache.set_views(wl.views())
+    n_splits = H.hw_debug_resolve(cache.ctx, 0, wl.n_workers)["n_splits"]
+    _say(f"w4_128k_sinks: automatic split count {n_splits}")
+    assert 1 < n_splits <= 255
+    for layer in range(2):
+        heads = _sink_heads(wl, layer)
+        assert any(35 <= h < 40 for h in heads)
+        _check_layer(cache, wl, layer, heads=heads)
     cache.close()
 
 
 def test_w4_128k_sinks_split256_sampled_heads():
+    # 256 partitions: beyond the 255 whose bounds ride in the launch arguments, so the
+    # uniform cuts p * n_groups / 256 (about two pages a partition).
     wl = W.make("w4_128k_sinks", n_layers=1)
     cache = make_cache(wl, max_splits=512)
     fill_layer(cache, wl, 0)
     cache.set_views(wl.views())
     H.hw_set_split(cache.ctx, 256)
     assert H.hw_debug_resolve(cache.ctx, 0, wl.n_workers)["n_splits"] == 256
-    rng = np.random.default_rng(wl.seed)
-    heads = sorted(set(int(x) for x in rng.choice(35, size=3, replace=False)) |
-                   {int(rng.integers(35, 40))})
-    _check_layer(cache, wl, 0, heads=heads)
+    _check_layer(cache, wl, 0, heads=_sink_heads(wl, 0))
     cache.close()

@@ -83,6 +83,9 @@ def test_workspace_size_formula(ctx):
     expect += al(al(16 * 4 * 4) + al(max_groups * 8 * 4))   # up to 8 ints per group descriptor
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
+    # step-plan region: counters (2 layers + overflow flag), block table, page lists,
+    # {d0, rate} offsets, 4-int descriptors
+    expect += al(al(3 * 4) + al(16 * 4 * 4) + al(16 * 4) + al(16 * 4 * 2 * 4) + al(max_groups * 4 * 4))
     assert H.hw_workspace_bytes(ctx) == expect
     # several query tokens per worker: partials for every (worker, token, head) row
     c3 = H.hw_create(make_cfg(max_query_tokens=3))
@@ -459,3 +462,58 @@ def test_partition_rejects_bad_arguments():
         with pytest.raises(H.HwError) as e:
             H.hw_debug_partition(*args)
         assert e.value.status == H.HW_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ step plans
+
+def test_step_plan_validation_before_any_change(ctx):
+    # hw_plan_steps checks its arguments before it needs the workspace or touches a page
+    with pytest.raises(H.HwError) as e:                      # no views yet
+        H.hw_plan_steps(ctx, 4, [1], [1], 0)
+    assert e.value.status == H.HW_ERR_STALE_VIEW
+    H.hw_debug_reserve(ctx, 0, [0, 1], [40, 7])
+    H.hw_debug_reserve(ctx, 1, [0, 1], [40, 7])
+    H.hw_set_views(ctx, [[0, 1]])
+    free0 = H.hw_free_pages(ctx)
+    bad = [
+        (dict(n_steps=0, ids=[1], tps=[1]), H.HW_ERR_INVALID_ARG),
+        (dict(n_steps=4, ids=[1, 1], tps=[1, 1]), H.HW_ERR_INVALID_ARG),
+        (dict(n_steps=4, ids=[99], tps=[1]), H.HW_ERR_INVALID_ARG),
+        (dict(n_steps=4, ids=[1], tps=[-1]), H.HW_ERR_INVALID_ARG),
+        (dict(n_steps=5000, ids=[1], tps=[1]), H.HW_ERR_INVALID_ARG),    # past max_position
+        (dict(n_steps=4, ids=[1], tps=[1]), H.HW_ERR_WORKSPACE),         # valid, no workspace
+    ]
+    for kw, status in bad:
+        with pytest.raises(H.HwError) as e:
+            H.hw_plan_steps(ctx, kw["n_steps"], kw["ids"], kw["tps"], 0)
+        assert e.value.status == status, kw
+        assert H.hw_free_pages(ctx) == free0
+    # explicit offsets or query positions cannot grow with the plan
+    H.hw_set_views(ctx, [[0, 1]], offsets=[[0, 40]])
+    with pytest.raises(H.HwError) as e:
+        H.hw_plan_steps(ctx, 4, [1], [1], 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    # lengths that differ between layers
+    H.hw_set_views(ctx, [[0, 1]])
+    H.hw_debug_reserve(ctx, 1, [1], [1])
+    with pytest.raises(H.HwError) as e:
+        H.hw_plan_steps(ctx, 4, [1], [1], 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG and "layers" in e.value.message
+    # no plan active: the step calls refuse
+    with pytest.raises(H.HwError) as e:
+        H.hw_append_step(ctx, 0, FAKE_K, FAKE_V, 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    with pytest.raises(H.HwError) as e:
+        H.hw_plan_end(ctx, 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+
+
+def test_step_plan_needs_bf16():
+    c = H.hw_create(make_cfg(kv_dtype=H.HW_F32))
+    H.hw_debug_reserve(c, 0, [0], [8])
+    H.hw_debug_reserve(c, 1, [0], [8])
+    H.hw_set_views(c, [[0]])
+    with pytest.raises(H.HwError) as e:
+        H.hw_plan_steps(c, 2, [0], [1], 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG and "bf16" in e.value.message
+    H.hw_destroy(c)
