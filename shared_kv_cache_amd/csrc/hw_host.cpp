@@ -20,6 +20,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -120,6 +121,9 @@ struct hw_ctx {
   bool event_live[kStagingSlots] = {};
   int next_slot = 0;
   bool debug_sync = false;
+
+  // device address of the static scratch on the context's device (hw_set_workspace)
+  void *scratch = nullptr;
 
   // profiling hooks: two events per recorded decode call
   std::vector<hipEvent_t> prof_events;
@@ -501,6 +505,27 @@ hw_status ensure_staging(hw_ctx *c) {
   return HW_OK;
 }
 
+// Per-device addresses of the static scratch (hw_kernels.hip), resolved with the device
+// current, once per device and process.
+std::mutex g_scratch_mu;
+void *g_scratch[256] = {};
+
+hw_status scratch_for_current_device(hw_ctx *c, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(c, e, "hipGetDevice");
+  if (dev < 0 || dev >= 256) return c->fail(HW_ERR_INVALID_ARG, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hw::scratch_address(&p);
+    if (e != hipSuccess || !p) return hip_fail(c, e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HW_OK;
+}
+
 hw_status post_launch(hw_ctx *c, hipError_t e, const char *what, hipStream_t s) {
   if (e != hipSuccess) return hip_fail(c, e, what);
   if (c->debug_sync) {
@@ -615,6 +640,9 @@ hw_status hw_set_workspace(hw_ctx *ctx, void *dev, size_t bytes) {
   // The pinned staging ring of the table uploads is allocated here, at set-up, so that no
   // append or decode allocates.
   hw_status sst = ensure_staging(ctx);
+  if (sst != HW_OK) return sst;
+  // The static scratch's address on this device, resolved once per device.
+  sst = scratch_for_current_device(ctx, &ctx->scratch);
   if (sst != HW_OK) return sst;
   ctx->ws = dev;
   ctx->ws_bytes = bytes;
@@ -940,6 +968,37 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
                                void *stream) {
   if (!ctx) return HW_ERR_INVALID_ARG;
   return decode_impl(ctx, layer, 1, q, out, lse, (hipStream_t)stream, workspace_partials(ctx));
+}
+
+hw_status hw_concurrent_decode_noalloc(hw_ctx *ctx, int32_t layer, const float *q, float *out,
+                                       float *lse, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  if (!ctx->ws || !ctx->scratch) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  if (!ctx->views.set) return ctx->fail(HW_ERR_STALE_VIEW, "no views set");
+  // The partials of the partition count this decode would use must fit the static scratch.
+  const int32_t n = ctx->views.n_workers;
+  const int32_t rows = rows_total(ctx, n);
+  int32_t splits = ctx->plan.active ? ctx->plan.splits : 0;
+  if (!splits) {
+    if (ctx->uploaded_valid && ctx->uploaded_sig == signature(ctx, layer)) {
+      splits = choose_splits(ctx, ctx->up_n_groups, rows);
+    } else {
+      Resolution r;
+      hw_status st = resolve(ctx, layer, r);
+      if (st != HW_OK) return st;
+      splits = choose_splits(ctx, (int32_t)r.g_page.size(), rows);
+    }
+  }
+  const size_t o_bytes = align_up((size_t)splits * g.n_kv_heads * rows * g.head_dim * sizeof(float));
+  const size_t need = o_bytes + (size_t)splits * g.n_kv_heads * rows * sizeof(float);
+  if (need > hw::kScratchBytes)
+    return ctx->fail(HW_ERR_WORKSPACE, "split partials need " + std::to_string(need) +
+                                           " bytes, more than the static scratch's " +
+                                           std::to_string(hw::kScratchBytes));
+  Partials part{reinterpret_cast<float *>(ctx->scratch),
+                reinterpret_cast<float *>((char *)ctx->scratch + o_bytes)};
+  return decode_impl(ctx, layer, 1, q, out, lse, (hipStream_t)stream, part);
 }
 
 hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q,

@@ -1187,6 +1187,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Static scratch of hw_concurrent_decode_noalloc: the split partials of a decode, in a
+// file-scope device array instead of the caller's workspace. Each GPU the library runs on
+// holds one copy until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, per device.
+// ------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)); }
+
+// ------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------
 

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 # every symbol the headers declare
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_concurrent_decode_tokens",
-           "hw_reset_block", "hw_plan_steps", "hw_append_step", "hw_plan_end",
+           "hw_concurrent_decode_noalloc", "hw_reset_block", "hw_plan_steps", "hw_append_step", "hw_plan_end",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
            "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
            "hw_debug_stream_read", "hw_debug_partition"]
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_concurrent_decode": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "hw_concurrent_decode_tokens": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                                 c_void_p, c_void_p]),
+        "hw_concurrent_decode_noalloc": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                                 c_void_p]),
         "hw_reset_block": (c_int, [c_void_p, c_int32]),
         "hw_plan_steps": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_void_p]),
         "hw_append_step": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
@@ -167,6 +169,13 @@ def hw_concurrent_decode_tokens(ctx, layer: int, n_new: int, q_ptr: int, out_ptr
     _check(ctx, load_library().hw_concurrent_decode_tokens(
         ctx, layer, n_new, c_void_p(q_ptr), c_void_p(out_ptr),
         c_void_p(lse_ptr) if lse_ptr else None, c_void_p(stream)))
+
+
+def hw_concurrent_decode_noalloc(ctx, layer: int, q_ptr: int, out_ptr: int,
+                                 lse_ptr: Optional[int], stream: int) -> None:
+    _check(ctx, load_library().hw_concurrent_decode_noalloc(
+        ctx, layer, c_void_p(q_ptr), c_void_p(out_ptr), c_void_p(lse_ptr) if lse_ptr else None,
+        c_void_p(stream)))
 
 
 def hw_reset_block(ctx, block_id: int) -> None:
