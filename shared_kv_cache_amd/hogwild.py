@@ -61,6 +61,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m shared_kv_cache_amd.build` "
                           "(there is no fallback path)")
+    # PyTorch ships its own HIP runtime under the same soname. Importing it first makes the
+    # library bind to that copy; loaded the other way round, the process would hold two HIP
+    # runtimes, and the second to initialise finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P32, P64 = POINTER(c_int32), POINTER(c_int64)
     sig = {
