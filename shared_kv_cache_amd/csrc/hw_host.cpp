@@ -77,6 +77,8 @@ struct Plan {
   int32_t rows = 0;                         // tokens per step over all planned blocks
   int32_t n_workers = 0, n_groups = 0, splits = 1;
   std::vector<int32_t> bounds;              // partition bounds (splits <= kMaxBoundSplits)
+  std::vector<hw::PlanBlock> append_blocks; // the planned append's launch arguments
+  std::vector<int32_t> append_pages;
 };
 
 }  // namespace
@@ -96,9 +98,9 @@ struct hw_ctx {
   size_t ws_bytes = 0;
   size_t off_trig = 0, off_freq = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0;
   size_t tables_bytes = 0;
-  // step-plan region: counters [n_layers] + overflow flag, block table, page lists,
-  // {d0, rate} offsets, 4-int group descriptors
-  size_t off_plan = 0, plan_cnt = 0, plan_blk = 0, plan_pages = 0, plan_delta = 0, plan_groups = 0;
+  // step-plan region: counters [n_layers] + overflow flag, {d0, rate} offsets, 4-int
+  // group descriptors
+  size_t off_plan = 0, plan_cnt = 0, plan_delta = 0, plan_groups = 0;
   Plan plan;
   size_t part_o_bytes = 0, part_lse_bytes = 0, total_bytes = 0;
 
@@ -175,10 +177,6 @@ void layout_workspace(hw_ctx *c) {
   size_t po = 0;
   c->plan_cnt = po;
   po = align_up(po + ((size_t)g.n_layers + 1) * sizeof(int32_t));
-  c->plan_blk = po;
-  po = align_up(po + (size_t)g.max_blocks * 4 * sizeof(int32_t));
-  c->plan_pages = po;
-  po = align_up(po + (size_t)g.n_pages * sizeof(int32_t));
   c->plan_delta = po;
   po = align_up(po + (size_t)g.max_blocks * g.max_workers * 2 * sizeof(int32_t));
   c->plan_groups = po;
@@ -1098,6 +1096,8 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
     rows += tokens_per_step[i];
   }
   if (rows > (1 << 20)) return ctx->fail(HW_ERR_INVALID_ARG, "too many tokens per step");
+  if (n_blocks > hw::kMaxPlanBlocks)
+    return ctx->fail(HW_ERR_INVALID_ARG, "a plan takes at most " + std::to_string(hw::kMaxPlanBlocks) + " blocks");
   // Every block of the views and of the plan must have the same length in every layer: one
   // set of tables serves all layers, each at its own count of planned appends.
   auto equal_layers = [&](int32_t b) {
@@ -1203,23 +1203,27 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
     bounds.resize((size_t)splits + 1);
     partition_bounds(seg_first.data(), n_groups, splits, split_alpha(ctx, rows_q), bounds.data());
   }
-  // Appends: {base length, tokens per step, first row, page-list offset} and the page lists.
-  std::vector<int32_t> btab, ptab;
+  // The planned append's launch arguments: per block {base length, tokens per step, first
+  // row, first page the window writes, where its id sits}, and the ids of the pages that
+  // the window's positions [base, base + n_steps * tps) fall in.
+  std::vector<hw::PlanBlock> ablk;
+  std::vector<int32_t> apages;
   int32_t row0 = 0;
   for (int32_t i = 0; i < n_blocks; ++i) {
-    btab.push_back((int32_t)len0(block_ids[i]));
-    btab.push_back(tokens_per_step[i]);
-    btab.push_back(row0);
-    btab.push_back((int32_t)ptab.size());
+    const int64_t base = len0(block_ids[i]);
+    const int32_t p0 = (int32_t)(base / g.page_size);
+    const int32_t p1 = grow[block_ids[i]] > 0 ? (int32_t)((cap(block_ids[i]) - 1) / g.page_size) : p0 - 1;
+    ablk.push_back(hw::PlanBlock{(int32_t)base, tokens_per_step[i], row0, p0, (int32_t)apages.size()});
+    for (int32_t q = p0; q <= p1; ++q) apages.push_back(pages[i][q]);
     row0 += tokens_per_step[i];
-    ptab.insert(ptab.end(), pages[i].begin(), pages[i].end());
   }
+  if (apages.size() > (size_t)hw::kMaxPlanPages)
+    return ctx->fail(HW_ERR_INVALID_ARG, "the plan's window spans more than " +
+                                             std::to_string(hw::kMaxPlanPages) + " pages");
   // One upload of the whole region, counters zeroed; the plan is set-up, not a step, so the
   // call waits for it.
   const size_t region = ctx->plan_groups + gtab.size() * sizeof(int32_t);
   std::vector<char> host(region, 0);
-  if (!btab.empty()) std::memcpy(host.data() + ctx->plan_blk, btab.data(), btab.size() * 4);
-  if (!ptab.empty()) std::memcpy(host.data() + ctx->plan_pages, ptab.data(), ptab.size() * 4);
   if (!dtab.empty()) std::memcpy(host.data() + ctx->plan_delta, dtab.data(), dtab.size() * 4);
   if (!gtab.empty()) std::memcpy(host.data() + ctx->plan_groups, gtab.data(), gtab.size() * 4);
   hipStream_t s = (hipStream_t)stream;
@@ -1251,6 +1255,8 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   p.n_groups = n_groups;
   p.splits = splits;
   p.bounds = std::move(bounds);
+  p.append_blocks = std::move(ablk);
+  p.append_pages = std::move(apages);
   ctx->uploaded_valid = false;
   return HW_OK;
 }
@@ -1271,8 +1277,8 @@ hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *
   a.k_src = k;
   a.v_src = v;
   a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
-  a.blocks = reinterpret_cast<const int32_t *>(base + ctx->plan_blk);
-  a.pages = reinterpret_cast<const int32_t *>(base + ctx->plan_pages);
+  std::copy(p.append_blocks.begin(), p.append_blocks.end(), a.blocks);
+  std::copy(p.append_pages.begin(), p.append_pages.end(), a.pages);
   a.step = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + layer;
   a.overflow = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + g.n_layers;
   a.n_blocks = (int32_t)p.blocks.size();

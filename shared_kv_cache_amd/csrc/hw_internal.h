@@ -59,39 +59,41 @@ struct AppendArgs {
 };
 
 struct DecodeArgs {
+  // The first 96 bytes hold what the decode kernel's prologue needs; it reads them in one
+  // batch of scalar loads (the offsets are checked by static_asserts in the kernel file).
   const void *k_layer;
   const void *v_layer;
   const float *q;          // [n_workers][n_q_heads][head_dim]
-  float *out;              // [n_workers][n_q_heads][head_dim]   (written when n_splits == 1)
-  float *lse;              // [n_workers][n_q_heads] or null      (idem)
   const int2 *groups;      // [n_groups] {group index of head 0, segment << 8 | valid tokens}
                            // (desc_stride 2); with the group's first local position as a
                            // third int (desc_stride 4, several query tokens per worker); or
                            // wide descriptors (desc_stride = kWideStride ints per group)
-  const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
   const double *turn_freq; // [head_dim/2] theta^(-2j/d) / (2 pi): rotation turns per position
-  float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
-  float *part_lse;         // [n_splits][n_kv_heads][rows] log2-domain partial normalisers
   int32_t n_groups;
-  int32_t n_workers;
-  int32_t n_q_heads;
-  int32_t n_kv_heads;
-  int32_t group;           // n_q_heads / n_kv_heads
-  int32_t rows;            // stacked rows per KV head: n_workers * n_new * group
   int32_t n_splits;
-  int32_t page_groups;
+  int32_t rows;            // stacked rows per KV head: n_workers * n_new * group
   int32_t rows_per_block;  // rows handled by one workgroup (grid z = row blocks)
+  int32_t group;           // n_q_heads / n_kv_heads
+  int32_t n_q_heads;
+  int32_t page_groups;
+  int32_t desc_stride;     // ints per group descriptor: 2, 4, or kWideStride (8-wave kernels only)
   float inv_group;         // 1 / group (rows < 2^22, so the query token of a row is exact in fp32)
+  float q_scale;           // softmax_scale * log2(e)
   float inv_rpw;           // 1 / (n_new * group): rows per worker
   int32_t n_new;           // query tokens per worker (rows = n_workers * n_new * group)
-  float q_scale;           // softmax_scale * log2(e)
-  // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
-  // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
-  int32_t split_begin[kMaxBoundSplits + 1];
-  int32_t desc_stride;     // ints per group descriptor: 2, 4, or kWideStride (8-wave kernels only)
+  int32_t n_workers;
+  int32_t n_kv_heads;
+  float *out;              // [n_workers][n_q_heads][head_dim]   (written when n_splits == 1)
+  float *lse;              // [n_workers][n_q_heads] or null      (idem)
+  const int32_t *delta;    // [n_segments][n_workers] query offset, -1 = not visible
+  float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
+  float *part_lse;         // [n_splits][n_kv_heads][rows] log2-domain partial normalisers
   // Step plan: the layer's counter of planned appends (null: no plan). Descriptors are then
   // {x, segment << 8, v0, rate} and delta holds {d0, rate} pairs (see the kernel).
   const int32_t *plan_step;
+  // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
+  // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
+  int32_t split_begin[kMaxBoundSplits + 1];
 };
 
 
@@ -99,15 +101,24 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 
 // The append of one planned step of one layer (a step plan, hw_plan_steps): every planned
 // block b takes its tokens_per_step tokens at local positions base(b) + s * tps(b) + j, s
-// being the layer's counter of planned appends, which the kernel then advances.
+// being the layer's counter of planned appends, which the kernel then advances. The
+// planned blocks and the ids of the pages the window writes ride in the launch arguments,
+// so that the only dependent loads are the counter and the rope table's rows.
+constexpr int kMaxPlanBlocks = 64;
+constexpr int kMaxPlanPages = 512;
+struct PlanBlock {
+  int32_t base;       // length when the plan began
+  int32_t tps;        // tokens per step
+  int32_t row0;       // first input row of the block's tokens
+  int32_t page0;      // index, in the block's page list, of the first page the window writes
+  int32_t pages_off;  // where that page's id sits in PlanAppendArgs::pages
+};
 struct PlanAppendArgs {
   void *k_layer;
   void *v_layer;
   const void *k_src;       // [rows][n_kv_heads][head_dim], rows in planned-block order
   const void *v_src;
   const float2 *trig;      // [max_position][head_dim/2] (cos, sin)
-  const int32_t *blocks;   // [n_blocks][4] {base length, tokens per step, first row, page-list offset}
-  const int32_t *pages;    // page lists of the planned blocks (capacity of the whole plan)
   int32_t *step;           // the layer's counter of planned appends
   int32_t *overflow;       // set to 1 by an append past the plan's last step (dropped)
   int32_t n_blocks;
@@ -116,6 +127,8 @@ struct PlanAppendArgs {
   int32_t n_kv_heads;
   int32_t page_size;
   int32_t page_groups;
+  PlanBlock blocks[kMaxPlanBlocks];
+  int32_t pages[kMaxPlanPages];
 };
 hipError_t launch_plan_append(hw_dtype dt, int head_dim, const PlanAppendArgs &a, hipStream_t s);
 struct MergeArgs {

@@ -156,11 +156,6 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
 // ------------------------------------------------------------------------------------
 template <typename KV, int D>
 __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
-  const int s = a.step[0];
-  if (s >= a.n_steps) {   // past the plan: nothing is written, the host reports it
-    if (threadIdx.x == 0) a.overflow[0] = 1;
-    return;
-  }
   constexpr int kChunks = D / 16;
   constexpr int kVec = 16 / (int)sizeof(KV);   // elements per 16-byte access
   static_assert(8 % kVec == 0, "8-element chunks in 16-byte accesses");
@@ -169,26 +164,27 @@ __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
   const KV *__restrict__ vsrc = static_cast<const KV *>(a.v_src);
   KV *__restrict__ kdst = static_cast<KV *>(a.k_layer);
   KV *__restrict__ vdst = static_cast<KV *>(a.v_layer);
+  const int s = a.step[0];
+  if (s >= a.n_steps) {   // past the plan: nothing is written, the host reports it
+    if (threadIdx.x == 0) a.overflow[0] = 1;
+    return;
+  }
   const int items = a.rows * hkv * kChunks;
   for (int it = threadIdx.x; it < items; it += blockDim.x) {
     const int c8 = it % kChunks;
     const int h = (it / kChunks) % hkv;
     const int r = it / (kChunks * hkv);
     int bi = 0;
-    for (int i = 0; i < a.n_blocks; ++i) {
-      const int r0 = a.blocks[4 * i + 2];
-      if (r >= r0 && r < r0 + a.blocks[4 * i + 1]) bi = i;
-    }
-    const int pos = a.blocks[4 * bi] + s * a.blocks[4 * bi + 1] + (r - a.blocks[4 * bi + 2]);
-    const int page = a.pages[a.blocks[4 * bi + 3] + pos / a.page_size];
+    for (int i = 0; i < a.n_blocks; ++i)
+      if (r >= a.blocks[i].row0 && r < a.blocks[i].row0 + a.blocks[i].tps) bi = i;
+    const PlanBlock &b = a.blocks[bi];
+    const int pos = b.base + s * b.tps + (r - b.row0);
+    const int page = a.pages[b.pages_off + pos / a.page_size - b.page0];
     const int t = pos % a.page_size;
-    const size_t grp = ((size_t)page * hkv + h) * a.page_groups + t / 32;
-    const int u = t & 31;
+    // Every load of the item, 16 bytes at a time, before any use: the 8 dims of the chunk
+    // in each half of the head for K and V, and the chunk's 8 (cos, sin) pairs.
     const size_t src = ((size_t)r * hkv + h) * D;
-    // Every load first, 16 bytes at a time: the 8 dims of the chunk in each half of the
-    // head, for K and V, and the chunk's 8 (cos, sin) pairs.
     uint4 kl[8 / kVec], kh[8 / kVec], vl[8 / kVec], vh[8 / kVec];
-    float4 cs[4];
 #pragma unroll
     for (int j = 0; j < 8 / kVec; ++j) {
       kl[j] = *reinterpret_cast<const uint4 *>(ksrc + src + 8 * c8 + kVec * j);
@@ -196,9 +192,12 @@ __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
       vl[j] = *reinterpret_cast<const uint4 *>(vsrc + src + 8 * c8 + kVec * j);
       vh[j] = *reinterpret_cast<const uint4 *>(vsrc + src + D / 2 + 8 * c8 + kVec * j);
     }
+    float4 cs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       cs[j] = reinterpret_cast<const float4 *>(a.trig + (size_t)pos * (D / 2) + 8 * c8)[j];
+    const size_t grp = ((size_t)page * hkv + h) * a.page_groups + t / 32;
+    const int u = t & 31;
     const KV *x0 = reinterpret_cast<const KV *>(kl), *x1 = reinterpret_cast<const KV *>(kh);
     const KV *w0 = reinterpret_cast<const KV *>(vl), *w1 = reinterpret_cast<const KV *>(vh);
     const float *cf = reinterpret_cast<const float *>(cs);
@@ -538,6 +537,14 @@ __device__ __forceinline__ void fetch_delta(int (&dl)[RT], int seg, const Decode
 
 __device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// A workgroup barrier for LDS only: it waits for this wave's LDS (and scalar) accesses, not
+// for its vector loads, so the K/V loads and stage fills in flight keep streaming across it.
+// (__syncthreads waits for every outstanding vector load first.) The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Segments whose rotated queries one phase of the cooperative rotation holds in LDS: about
 // 64 KiB of operands.
 template <typename KV, int D, int RT>
@@ -545,6 +552,65 @@ constexpr int phase_segments() {
   constexpr int per_seg = RT * (D / 32) * 64 * (int)sizeof(typename Frag<KV, D>::QOp);
   constexpr int c = (64 * 1024) / per_seg;
   return c < 1 ? 1 : (c > 16 ? 16 : c);
+}
+
+// The launch arguments the decode prologue needs (the first 96 bytes of DecodeArgs, and the
+// workgroup's two partition bounds), read with three scalar loads that go out together and
+// one wait, instead of one round trip per field as each is first used.
+typedef int i32x16a __attribute__((ext_vector_type(16), aligned(4)));
+typedef int i32x8a __attribute__((ext_vector_type(8), aligned(4)));
+typedef int i32x2a __attribute__((ext_vector_type(2), aligned(4)));
+static_assert(offsetof(DecodeArgs, k_layer) == 0 && offsetof(DecodeArgs, v_layer) == 8 &&
+                  offsetof(DecodeArgs, q) == 16 && offsetof(DecodeArgs, groups) == 24 &&
+                  offsetof(DecodeArgs, turn_freq) == 32 && offsetof(DecodeArgs, n_groups) == 40 &&
+                  offsetof(DecodeArgs, n_splits) == 44 && offsetof(DecodeArgs, rows) == 48 &&
+                  offsetof(DecodeArgs, rows_per_block) == 52 && offsetof(DecodeArgs, group) == 56 &&
+                  offsetof(DecodeArgs, n_q_heads) == 60 && offsetof(DecodeArgs, page_groups) == 64 &&
+                  offsetof(DecodeArgs, desc_stride) == 68 && offsetof(DecodeArgs, inv_group) == 72 &&
+                  offsetof(DecodeArgs, split_begin) % 4 == 0,
+              "DecodeArgs layout read by load_head");
+struct Head {
+  const void *k_layer, *v_layer;
+  const float *q;
+  const int2 *groups;
+  const double *turn_freq;
+  int n_groups, n_splits, rows, rows_per_block, group, n_q_heads, page_groups, desc_stride;
+  float inv_group;
+  int sb0, sb1;   // split_begin[sp], split_begin[sp + 1]
+};
+// A device pointer rebuilt from its two halves, marked global (address space 1), so that the
+// accesses through it stay global loads: as a plain generic pointer they would become flat
+// loads, which also count on lgkmcnt and serialise with the scalar loads.
+__device__ __forceinline__ const void *ptr_of(int lo, int hi) {
+  typedef __attribute__((address_space(1))) const char GChar;
+  return (const void *)(GChar *)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ Head load_head(int sp) {
+  typedef __attribute__((address_space(4))) const i32x16a C16;
+  typedef __attribute__((address_space(4))) const i32x8a C8;
+  typedef __attribute__((address_space(4))) const i32x2a C2;
+  const ConstInt *kp = (const ConstInt *)__builtin_amdgcn_kernarg_segment_ptr();
+  const i32x16a h0 = *(C16 *)kp;
+  const i32x8a h1 = *(C8 *)(kp + 16);
+  const i32x2a sb = *(C2 *)(kp + offsetof(DecodeArgs, split_begin) / 4 + sp);
+  Head h;
+  h.k_layer = ptr_of(h0[0], h0[1]);
+  h.v_layer = ptr_of(h0[2], h0[3]);
+  h.q = static_cast<const float *>(ptr_of(h0[4], h0[5]));
+  h.groups = static_cast<const int2 *>(ptr_of(h0[6], h0[7]));
+  h.turn_freq = static_cast<const double *>(ptr_of(h0[8], h0[9]));
+  h.n_groups = h0[10];
+  h.n_splits = h0[11];
+  h.rows = h0[12];
+  h.rows_per_block = h0[13];
+  h.group = h0[14];
+  h.n_q_heads = h0[15];
+  h.page_groups = h1[0];
+  h.desc_stride = h1[1];
+  h.inv_group = __int_as_float(h1[2]);
+  h.sb0 = sb[0];
+  h.sb1 = sb[1];
+  return h;
 }
 
 // One workgroup = one (split, KV head, block of up to 16 * RT rows), NW waves. Every wave
@@ -614,7 +680,6 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   __shared__ double sm_freq[D / 2];
   __shared__ float sm_m[NW][16 * RT];
   __shared__ float sm_l[NW][16 * RT];
-  __shared__ float sm_rowm[64], sm_rowl[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -624,30 +689,61 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // in turn, so with 8 KV heads each XCD takes one head's partitions, the same mix of the
   // group list on every XCD.
   const int kvh = blockIdx.x, split = blockIdx.y;
-  const int row0 = blockIdx.z * a.rows_per_block;
-  const int nrows = min(a.rows_per_block, a.rows - row0);
+  const int sp = split < kMaxBoundSplits ? split : kMaxBoundSplits - 1;
+  const Head hd = load_head(sp);
+  const int row0 = blockIdx.z * hd.rows_per_block;
+  const int nrows = min(hd.rows_per_block, hd.rows - row0);
   QOp *qt = reinterpret_cast<QOp *>(smem + (LDSST ? 0 : Q_FLOATS));
   QOp *qop_wave = qt + (size_t)wave * RT * NC * 64;   // NST = 1 without LDSST: this wave's operands
   // LDSST: this wave's stage, NLOAD slots of 64 lanes x 16 bytes
   uint4 (*stage)[64] = reinterpret_cast<uint4 (*)[64]>(smem + QT_FLOATS) + wave * NLOAD;
   QOp qreg[RT][NC];   // LDSST: the rotated query operands of the current segment
 
-  // This workgroup's token groups [begin, end); this wave's contiguous run of them.
-  const bool bounded = a.n_splits <= kMaxBoundSplits;
-  const long long begin = bounded ? a.split_begin[split] : (long long)split * a.n_groups / a.n_splits;
-  const long long end = bounded ? a.split_begin[split + 1] : (long long)(split + 1) * a.n_groups / a.n_splits;
-  const long long wfirst = begin + (end - begin) * wave / NW;
-  const long long wcount = begin + (end - begin) * (wave + 1) / NW - wfirst;
-  const long long wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);
-  const KV *kl = static_cast<const KV *>(a.k_layer);
-  const KV *vl = static_cast<const KV *>(a.v_layer);
-  const size_t head_groups = (size_t)kvh * a.page_groups;
-
   // Stacked row rr = (query token wt, head rr - wt * group of the KV head's group) with
   // wt = rr / group, and query token wt = (worker wt / n_new, token wt % n_new): both
   // quotients as floor((x + 0.5) * (1 / y)) in fp32, exact while rr < 2^22 (the error of
   // the product stays below 0.5 / y). With one token per worker, wt is the worker.
-  auto tok_of = [&](int rr) { return (int)(((float)rr + 0.5f) * a.inv_group); };
+  const float inv_group = hd.inv_group;
+  auto tok_of = [=](int rr) { return (int)(((float)rr + 0.5f) * inv_group); };
+
+  // Prologue, ordered for latency. The raw queries and the rotation frequencies go out
+  // first: they need only launch arguments, and are in flight before the first K/V loads
+  // of every wave flood the memory system (the queries gate the barrier before the first
+  // group is computed).
+  // Loads are unconditional (a padding row reads row 0 of the block, zeroed at staging), so
+  // that no wait is needed until the values are staged.
+  constexpr int QV4 = (RT * 16 * D / 4 + NT - 1) / NT;   // float4 of queries per thread
+  float4 qv[QV4];
+  bool qok[QV4];
+#pragma unroll
+  for (int k = 0; k < QV4; ++k) {
+    const int i = tid + k * NT;                      // float4 index in [RT*16][D/4]
+    qok[k] = i < RT * 16 * D / 4 && i / (D / 4) < nrows;
+    const int r = qok[k] ? i / (D / 4) : 0, d4 = i % (D / 4);
+    const int rr = row0 + r;
+    const int wt = tok_of(rr), gq = rr - wt * hd.group;
+    qv[k] = reinterpret_cast<const float4 *>(hd.q + ((size_t)wt * hd.n_q_heads + kvh * hd.group + gq) * D)[d4];
+  }
+  const double fq = hd.turn_freq[tid % (D / 2)];
+
+  // This workgroup's token groups [begin, end); this wave's contiguous run of them. Both
+  // launch-argument bounds are read unconditionally, so that the scalar loads go out in one
+  // batch instead of one round trip after another.
+  // Beyond kMaxBoundSplits partitions, the uniform cuts floor(p * n_groups / n_splits) in
+  // fp64 (exact: the product stays far below 2^53).
+  const int n_splits = hd.n_splits, n_groups = hd.n_groups;
+  int begin = hd.sb0, end = hd.sb1;
+  if (n_splits > kMaxBoundSplits) {
+    begin = (int)((double)split * n_groups / n_splits);
+    end = (int)((double)(split + 1) * n_groups / n_splits);
+  }
+  const int wfirst = begin + (int)((long long)(end - begin) * wave / NW);
+  const int wcount = begin + (int)((long long)(end - begin) * (wave + 1) / NW) - wfirst;
+  const int wlast = wfirst + (wcount > 0 ? wcount - 1 : 0);
+  const KV *kl = static_cast<const KV *>(hd.k_layer);
+  const KV *vl = static_cast<const KV *>(hd.v_layer);
+  const size_t head_groups = (size_t)kvh * hd.page_groups;
+
   auto worker_of = [&](int rr) {
     if constexpr (MT) return (int)(((float)rr + 0.5f) * a.inv_rpw);
     else return tok_of(rr);
@@ -678,10 +774,10 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   const int wlo = __builtin_amdgcn_readfirstlane(worker_of(row0));
   const int nw = __builtin_amdgcn_readfirstlane(worker_of(row0 + nrows - 1)) - wlo + 1;
 
-  // Prologue, ordered for latency. Scalar loads first: this wave's first descriptors (and,
-  // COOP, the workgroup's segment range). Then the raw queries and rotation frequencies,
-  // the offsets (of the first phase, or of this wave's first two groups) and group 0's K/V;
-  // only then the waits for the queries and offsets, which leave the K/V loads in flight.
+  // Then the scalar loads of this wave's first descriptors (and, COOP, the workgroup's
+  // segment range), the offsets (of the first phase, or of this wave's first two groups)
+  // and group 0's K/V; only then the waits for the queries and offsets, which leave the
+  // K/V loads in flight.
   // A fetch with nothing to fetch (no group for this wave, or past the end of its run)
   // still issues its loads, from descriptor (0, 0): page 0 of the head and the first row of
   // the offset table, both always allocated; the data goes unused. Loads issued
@@ -691,38 +787,34 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   if constexpr (PLAN) pstep = *(const ConstInt *)a.plan_step;
   int s_lo = 0, s_hi = -1;
   if (COOP && end > begin) {
-    s_lo = load_desc<MT>(a.groups, begin, a.desc_stride).y >> 8;
-    s_hi = load_desc<MT>(a.groups, end - 1, a.desc_stride).y >> 8;   // (segments: no plan term)
+    s_lo = load_desc<MT>(hd.groups, begin, hd.desc_stride).y >> 8;
+    s_hi = load_desc<MT>(hd.groups, end - 1, hd.desc_stride).y >> 8;   // (segments: no plan term)
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   GDesc desc, next, next2;
   // WIDE: the offsets of workers 0.. for the segments of desc, next, next2
   WideOff ow, ow_next, ow_next2;
   auto desc_at = [&](long long i, WideOff &off) __attribute__((always_inline)) {
-    if constexpr (WIDE) return load_desc_wide(a.groups, i, off);
-    else return load_desc<MT, PLAN>(a.groups, i, a.desc_stride, pstep);
+    if constexpr (WIDE) return load_desc_wide(hd.groups, i, off);
+    else return load_desc<MT, PLAN>(hd.groups, i, hd.desc_stride, pstep);
   };
-  if (wcount > 0) desc = desc_at(wfirst, ow);   // only groups of this wave's run
-  if (wcount > 1) next = desc_at(wfirst + 1, ow_next);
+  // The first three descriptors of this wave's run, loaded unconditionally (indices clamped
+  // into the list) so that the three loads go out together; a descriptor past the run is then
+  // replaced by (0, 0).
+  {
+    const int lastg = n_groups > 0 ? n_groups - 1 : 0;
+    desc = desc_at(min(wfirst, lastg), ow);
+    next = desc_at(min(wfirst + 1, lastg), ow_next);
+    next2 = desc_at(min(wfirst + 2, lastg), ow_next2);
+    if (wcount <= 0) desc = GDesc();
+    if (wcount <= 1) next = GDesc();
+    if (wcount <= 2) next2 = GDesc();
+  }
   // WIDE: the lane's rows' offsets (all rows in one block: worker index = row_w)
   auto wide_rows = [&](int (&dl)[RT], const WideOff &off) __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) dl[rt] = wide_pick(off, row_w[rt]);
   };
-  constexpr int QV4 = (RT * 16 * D / 4 + NT - 1) / NT;   // float4 of queries per thread
-  float4 qv[QV4];
-#pragma unroll
-  for (int k = 0; k < QV4; ++k) {
-    const int i = tid + k * NT;                      // float4 index in [RT*16][D/4]
-    const int r = i / (D / 4), d4 = i % (D / 4);
-    qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < RT * 16 * D / 4 && r < nrows) {
-      const int rr = row0 + r;
-      const int wt = tok_of(rr), gq = rr - wt * a.group;
-      qv[k] = reinterpret_cast<const float4 *>(a.q + ((size_t)wt * a.n_q_heads + kvh * a.group + gq) * D)[d4];
-    }
-  }
-  const double fq = tid < D / 2 ? a.turn_freq[tid] : 0.0;
   // COOP: offsets of the phase starting at segment seg_lo: sm_dl[s * nw + k] = delta of
   // worker wlo + k for segment seg_lo + s (-1: the block is not in that worker's view).
   constexpr int DLPT = COOP ? (CAP * NWMAX + NT - 1) / NT : 1;
@@ -746,6 +838,9 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     load_offsets(s_lo);
     fetch_group(st2, desc, kl, vl, head_groups, lane);
   } else if constexpr (WIDE) {
+    // LDSST: the queries land before group 0 is requested, ahead of the flood of every
+    // wave's K/V loads (they gate the barrier below)
+    if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     fetch_group(st, desc, kl, vl, head_groups, lane);
     wide_rows(dl_cur, ow);
   } else {
@@ -753,21 +848,20 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     fetch_group(st, desc, kl, vl, head_groups, lane);
     fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
   }
-  if (wcount > 2) next2 = desc_at(wfirst + 2, ow_next2);
   // Stage the queries, pre-scaled by softmax_scale * log2(e), the offsets and the rotation
   // frequencies in turns per position.
 #pragma unroll
   for (int k = 0; k < QV4; ++k) {
     const int i = tid + k * NT;
     if (i < RT * 16 * D / 4) {
-      const float4 x = qv[k];
+      const float4 x = qok[k] ? qv[k] : make_float4(0.f, 0.f, 0.f, 0.f);
       *reinterpret_cast<float4 *>(qrows + (i / (D / 4)) * QSTRIDE + (i % (D / 4)) * 4) =
           make_float4(x.x * a.q_scale, x.y * a.q_scale, x.z * a.q_scale, x.w * a.q_scale);
     }
   }
   if constexpr (COOP) store_offsets();
   if (tid < D / 2) sm_freq[tid] = fq;
-  __syncthreads();
+  lds_barrier();   // the first groups' loads stay in flight
 
   // Rotation of one row's query by delta = q_pos(w) - offset(w, block), for the 8 pairs
   // (j, j + D/2), j = j0 .. j0 + 7: the angle delta * theta_j is reduced to a fraction of a
@@ -828,10 +922,12 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // One group: visibility and (NST = 1, new segment) rotation, scores, online softmax, PV.
   // seg_lo: first segment of the current phase (COOP); delta: the lane's rows' offsets for
   // the group's block (NST = 1).
-  auto process = [&](S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
+  // Entering a group: its rows' visibility of the group's block and, when the block is new
+  // to the wave (NST = 1), the rotation of the rows' queries. The rotation reads LDS, and
+  // the compiler makes an LDS read wait for every LDS-DMA fill in flight, so the staged
+  // loop enters a group before it issues the next fill.
+  auto enter = [&](const S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
     const int seg = sg.desc_y >> 8;
-    const int nvalid = sg.desc_y & 255;
-    const QOp *qs;
     if constexpr (COOP) {
       const int sl = seg - seg_lo;                   // segment within the phase
       if (seg != cur_seg) {
@@ -844,7 +940,6 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
           rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
         }
       }
-      qs = qt + (size_t)sl * RT * NC * 64 + lane;
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -875,8 +970,14 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
           }
         }
       }
-      qs = qop_wave + lane;
     }
+  };
+
+  // One group after enter: scores, online softmax, PV.
+  auto compute = [&](S &sg, int seg_lo) __attribute__((always_inline)) {
+    const int seg = sg.desc_y >> 8;
+    const int nvalid = sg.desc_y & 255;
+    const QOp *qs = COOP ? qt + (size_t)(seg - seg_lo) * RT * NC * 64 + lane : qop_wave + lane;
 
     // Scores of the 32 tokens for every row: lane (row col, group grp) gets tokens
     // 8*grp + 4*hh + r of row tile rt in sc[rt][hh][r].
@@ -959,11 +1060,16 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = sg.f.pv(dt, pop, o[rt][dt]);
     }
   };
+  auto process = [&](S &sg, int seg_lo, const int (&delta)[RT]) __attribute__((always_inline)) {
+    enter(sg, seg_lo, delta);
+    compute(sg, seg_lo);
+  };
 
   if constexpr (LDSST) {
-    // Group 0 is in registers; group 1 streams into the stage now (after the barrier above:
-    // a barrier waits for outstanding LDS fills). Group i >= 1 is read from the stage, the
-    // fill of group i+1 issued, then group i computed. The compiler does not order stage
+    // Group 0 is in registers; group 1 streams into the stage now, after the queries' LDS
+    // writes (the compiler waits for every vector load, fills included, before an LDS
+    // write that follows a fill). Group i >= 1 is read from the stage, the fill of group
+    // i+1 issued, then group i computed. The compiler does not order stage
     // reads after fills or count fills in its waits, so the waits are explicit: a fill is
     // the only vector load in flight when the stage is read (vmcnt(0) waits for exactly it),
     // and the stage read completes before the refill. Group 0 is computed outside the loop
@@ -972,6 +1078,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // A wave raises its priority while it takes its group from the stage and issues the next
     // fill, and drops it to compute: the other wave on the SIMD, mid-compute, then yields
     // the issue slots to the one whose data has landed, which keeps the fills going.
+    if (wcount > 0) enter(st, 0, dl_cur);   // the first rotation, before any fill
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     if (wcount > 1) {
       const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
@@ -979,8 +1087,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-    if (wcount > 0) process(st, 0, dl_cur);
-    for (long long i = 1; i < wcount; ++i) {
+    if (wcount > 0) compute(st, 0);
+    for (int i = 1; i < wcount; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // group i's fill has landed
@@ -989,23 +1097,25 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       st.desc_y = next.y;
       st.desc_ls = next.ls;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage read before it is refilled
+      next = next2;                                         // group i + 1
+      ow = ow_next;
+      ow_next = ow_next2;
+      wide_rows(dl_cur, ow);                                // group i's offsets
+      enter(st, 0, dl_cur);
+      __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < wcount) {
-        const size_t gb = ((size_t)next2.x + head_groups) * (size_t)(32 * D);
+        const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
         F::load_lds(kl + gb, vl + gb, lane, stage);
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      next = next2;
-      ow = ow_next;
-      ow_next = ow_next2;
-      wide_rows(dl_cur, ow);
       next2 = desc_at(min(wfirst + i + 2, wlast), ow_next2);
-      process(st, 0, dl_cur);
+      compute(st, 0);
     }
   } else if constexpr (!COOP) {
     // Group i: its descriptor and offsets came with group i-1; group i+1's descriptor is
     // in and group i+2's on its way.
-    for (long long i = 0; i < wcount; ++i) {
+    for (int i = 0; i < wcount; ++i) {
       if (i > 0) {
         desc = next;
         next = next2;
@@ -1028,17 +1138,17 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // them. Group i is in flight in st2 when its step starts; it moves to st and group i+1
     // (descriptor next, in since the last step) is issued into st2 before group i is
     // computed; group i+2's descriptor is on its way.
-    long long i = 0;
+    int i = 0;
     for (int ph = 0; ph < nph; ++ph) {
       const int seg_lo = s_lo + ph * CAP;
       if (ph > 0) {
-        __syncthreads();                             // the previous phase's table is done
+        lds_barrier();                               // the previous phase's table is done
         load_offsets(seg_lo);
         store_offsets();
-        __syncthreads();
+        lds_barrier();
       }
       rotate_phase(min(CAP, s_hi + 1 - seg_lo));
-      __syncthreads();
+      lds_barrier();
       while (i < wcount && (desc.y >> 8) < seg_lo + CAP) {
         st = st2;
         fetch_group(st2, i + 1 < wcount ? next : GDesc(), kl, vl, head_groups, lane);
@@ -1051,12 +1161,18 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     }
   }
 
-  // ---- combine the waves: common max, then one LDS pass in which every slot is summed
-  // over the waves in a fixed order ----
+  // ---- combine the waves: each wave leaves its (m, l) per row and its raw O in LDS, then
+  // every slot of the output is summed over the waves in a fixed order, each wave's part
+  // scaled to the common maximum (results do not depend on timing) ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) l[rt] = wave_sum_across_groups(l[rt]);
-  if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no fill in flight
-  __syncthreads();  // every wave is done with the staged queries and operands
+  // LDSST: a wave's O goes into its own stage (no other wave touches it) once its last fill
+  // has landed; otherwise into smem, once every wave is done with the queries staged there.
+  constexpr int WSTRIDE = LDSST ? NLOAD * 64 : SLOTS;   // f32x4 slots between waves' parts
+  static_assert(!LDSST || NLOAD * 64 >= SLOTS, "a wave's O fits its stage");
+  if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else lds_barrier();
+  f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
   if (grp == 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -1064,39 +1180,29 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       sm_l[wave][rt * 16 + col] = l[rt];
     }
   }
-  __syncthreads();
-  f32x4 *buf = reinterpret_cast<f32x4 *>(smem);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + col;
-    float mm = -INFINITY;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int t = 0; t < NW; ++t) mm = fmaxf(mm, sm_m[t][r]);
-    const float fac = m[rt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[rt] - mm);
-    if (wave == 0 && grp == 0) {
-      float ll = 0.0f;
-#pragma unroll
-      for (int t = 0; t < NW; ++t) {
-        const float mw = sm_m[t][r];
-        ll += mw == -INFINITY ? 0.0f : sm_l[t][r] * __builtin_amdgcn_exp2f(mw - mm);
-      }
-      sm_rowm[r] = mm;
-      sm_rowl[r] = ll;
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) buf[wave * SLOTS + (rt * NDT + dt) * 64 + lane] = o[rt][dt] * fac;
-  }
-  __syncthreads();
+    for (int dt = 0; dt < NDT; ++dt) buf[wave * WSTRIDE + (rt * NDT + dt) * 64 + lane] = o[rt][dt];
+  lds_barrier();
 
   const bool direct = a.n_splits == 1;
   for (int q = tid; q < SLOTS; q += NT) {
     const int rt = q / (NDT * 64), dt = (q / 64) % NDT, ln = q % 64;
     const int r = rt * 16 + (ln & 15);
     if (r >= nrows) continue;
-    f32x4 x = buf[q];
+    float mm = -INFINITY;
 #pragma unroll
-    for (int t = 1; t < NW; ++t) x += buf[t * SLOTS + q];
-    const float L = sm_rowl[r];
+    for (int t = 0; t < NW; ++t) mm = fmaxf(mm, sm_m[t][r]);
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      const float mt = sm_m[t][r];
+      const float f = mt == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt - mm);
+      x += buf[t * WSTRIDE + q] * f;
+      L += sm_l[t][r] * f;
+    }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int rr = row0 + r;
     float *dst;
@@ -1105,11 +1211,11 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       dst = a.out + ((size_t)wt * a.n_q_heads + h) * D;
       if (dt == 0 && (ln >> 4) == 0 && a.lse)
         a.lse[(size_t)wt * a.n_q_heads + h] =
-            L > 0.0f ? (sm_rowm[r] + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+            L > 0.0f ? (mm + __log2f(L)) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t prow = ((size_t)split * a.n_kv_heads + kvh) * a.rows + rr;
       dst = a.part_o + prow * D;
-      if (dt == 0 && (ln >> 4) == 0) a.part_lse[prow] = L > 0.0f ? sm_rowm[r] + __log2f(L) : -INFINITY;
+      if (dt == 0 && (ln >> 4) == 0) a.part_lse[prow] = L > 0.0f ? mm + __log2f(L) : -INFINITY;
     }
     *reinterpret_cast<float4 *>(dst + 16 * dt + 4 * (ln >> 4)) =
         make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
@@ -1119,21 +1225,22 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
 // ------------------------------------------------------------------------------------
 // lse_merge: four lanes per (worker, query head, 4 output dims); lane j of the four merges
 // partials j, j+4, ... with all of its loads in flight together, and the four running
-// results are combined with lane exchanges.
+// results are combined with lane exchanges. Workgroup b serves KV head b mod n_kv_heads:
+// dispatch deals workgroups to the 8 XCDs in turn, as it dealt the decode's workgroups
+// (KV head fastest), so a head's partials are merged on the XCD whose L2 they were
+// written through.
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   constexpr int Q4 = D / 4;
   constexpr int B = 8;   // partials per lane whose loads are in flight together
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int sub = t & 3;
-  const int item = t >> 2;
-  const bool live = item < a.n_workers * a.n_q_heads * Q4;
+  const int kvh = blockIdx.x % a.n_kv_heads;
+  const int item = (blockIdx.x / a.n_kv_heads) * 64 + (threadIdx.x >> 2);   // in this KV head
+  const int sub = threadIdx.x & 3;
+  const bool live = item < a.rows * Q4;
   const int it = live ? item : 0;
-  const int row = it / Q4, q4 = it % Q4;
-  const int w = row / a.n_q_heads, h = row % a.n_q_heads;
-  const int kvh = h / a.group;
-  const int rr = w * a.group + h % a.group;
+  const int rr = it / Q4, q4 = it % Q4;        // stacked row (query token, head of the group)
+  const int w = rr / a.group, h = kvh * a.group + rr % a.group;
   const size_t stride = (size_t)a.n_kv_heads * a.rows;
   const size_t base = (size_t)kvh * a.rows + rr;
   float mm = -INFINITY, tot = 0.0f;
@@ -1318,8 +1425,8 @@ hipError_t launch_stream_read(const void *src, size_t bytes, float *sink, int n_
 }
 
 hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s) {
-  const int threads = 4 * a.n_workers * a.n_q_heads * (head_dim / 4);
-  dim3 grid((threads + 255) / 256), block(256);
+  const int per_head = (a.rows * (head_dim / 4) + 63) / 64;   // workgroups of 64 items
+  dim3 grid(per_head * a.n_kv_heads), block(256);
   if (head_dim == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, block, 0, s, a);
   return hipGetLastError();

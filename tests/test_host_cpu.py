@@ -83,9 +83,9 @@ def test_workspace_size_formula(ctx):
     expect += al(al(16 * 4 * 4) + al(max_groups * 8 * 4))   # up to 8 ints per group descriptor
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
-    # step-plan region: counters (2 layers + overflow flag), block table, page lists,
-    # {d0, rate} offsets, 4-int descriptors
-    expect += al(al(3 * 4) + al(16 * 4 * 4) + al(16 * 4) + al(16 * 4 * 2 * 4) + al(max_groups * 4 * 4))
+    # step-plan region: counters (2 layers + overflow flag), {d0, rate} offsets, 4-int
+    # descriptors
+    expect += al(al(3 * 4) + al(16 * 4 * 2 * 4) + al(max_groups * 4 * 4))
     assert H.hw_workspace_bytes(ctx) == expect
     # several query tokens per worker: partials for every (worker, token, head) row
     c3 = H.hw_create(make_cfg(max_query_tokens=3))
