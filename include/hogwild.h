@@ -216,8 +216,9 @@ hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new,
  * number of steps taken: each block's length, each group's token count and each (worker,
  * block) query offset (the sum of the lengths from that block to the end of the worker's
  * view, minus one). A step plan resolves the views once for a window of n_steps steps and
- * keeps, per layer, a device-side count of the planned appends done; hw_append_step
- * advances it and the decode kernel derives the step's group sizes and offsets from it.
+ * keeps, per layer, a device-side count of the planned steps done; the append and the
+ * decode kernels derive the step's positions, group sizes and offsets from it, and the
+ * decode's last kernel advances it.
  * A step (per layer: hw_append_step, then hw_concurrent_decode) then performs no host-side
  * resolution, no staging wait and no copy: it can be captured once as a HIP graph and
  * replayed for each step of the window.
@@ -235,7 +236,8 @@ hw_status hw_concurrent_decode_tokens(hw_ctx *ctx, int32_t layer, int32_t n_new,
  * tables, hw_concurrent_decode_tokens takes n_new = 1 only, and hw_block_info reports the
  * lengths the blocks had when the plan began.
  * Errors: HW_ERR_INVALID_ARG (a plan already active, fp32 pools, explicit offsets or q_pos,
- * ids, counts, lengths that differ between layers, a block that would reach max_position),
+ * ids, counts, lengths that differ between layers, a block that would reach max_position;
+ * more than 64 planned blocks, 1024 tokens per step or 512 pages written in the window),
  * HW_ERR_STALE_VIEW (no views, or a view that would reach max_position within the window),
  * HW_ERR_OUT_OF_PAGES, HW_ERR_WORKSPACE, HW_ERR_HIP; on any error nothing changed. Not
  * capturable (it uploads and waits). */
@@ -247,16 +249,21 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
  * [head_dim] bf16, raw, 16-byte aligned, rows = sum of tokens_per_step, in the plan's
  * block order. Planned
  * block i's tokens go to local positions base_i + s * tokens_per_step[i] + j, s being the
- * number of planned appends this layer has had, written as hw_append_kv writes them; then
- * the layer's count advances. One workgroup does the whole append (meant for a few tokens
- * per step). An append past the window's n_steps writes nothing and is reported by
- * hw_plan_end. Capturable: enqueues one kernel, reads nothing from the host.
- * Errors: HW_ERR_INVALID_ARG (no plan, layer, NULL or misaligned k/v), HW_ERR_HIP. */
+ * number of planned steps this layer has completed, written as hw_append_kv writes them
+ * (one workgroup per token). The layer's next hw_concurrent_decode attends over them and,
+ * after its kernels have read the count, advances it (with the split merge, or a one-thread
+ * kernel when the decode needs no merge): a layer's planned step is hw_append_step then
+ * hw_concurrent_decode, and a decode without an append before it sees the count as it is.
+ * An append past the window's n_steps writes nothing and is reported by hw_plan_end.
+ * Capturable: enqueues one kernel and reads nothing from the host.
+ * Errors: HW_ERR_INVALID_ARG (no plan, layer, NULL or misaligned k/v, or a second append of
+ * the layer before its decode), HW_ERR_HIP. */
 hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, void *stream);
 
 /* End the active plan: waits for `stream`, reads the device's per-layer counts of planned
- * appends back, sets every planned block's length in each layer to base + count *
- * tokens_per_step, and returns the pages the blocks did not fill to the free list. Views
+ * steps back (a layer appended but not yet decoded counts its append), sets every planned
+ * block's length in each layer to base + count * tokens_per_step, and returns the pages
+ * the blocks did not fill to the free list. Views
  * and tables are then as without a plan (the next decode uploads fresh tables).
  * Errors: HW_ERR_INVALID_ARG if no plan is active, or if some layer had more planned appends
  * than n_steps (the extra appends were dropped; the plan is ended all the same); HW_ERR_HIP. */

@@ -79,6 +79,9 @@ struct Plan {
   std::vector<int32_t> bounds;              // partition bounds (splits <= kMaxBoundSplits)
   std::vector<hw::PlanBlock> append_blocks; // the planned append's launch arguments
   std::vector<int32_t> append_pages;
+  // per layer: 1 while the step's append is enqueued and its decode not yet (the layer's
+  // counter advances after that decode)
+  std::vector<uint8_t> pending;
 };
 
 }  // namespace
@@ -750,6 +753,8 @@ struct DecodeTables {
   int32_t n_groups = 0, stride = 2, splits = 1;
   const int32_t *bounds = nullptr;      // splits + 1 cuts, or null: uniform cuts
   const int32_t *plan_step = nullptr;   // step plans: the layer's counter of planned appends
+  int32_t plan_pending = 0, plan_n_steps = 0;
+  int32_t *advance = nullptr;           // counter to advance once the decode has read it
 };
 
 // Split partials of a decode: the workspace's, or a caller-provided buffer of the same shape.
@@ -799,6 +804,8 @@ hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const f
   a.q_scale = (float)((double)g.softmax_scale * 1.4426950408889634);
   a.desc_stride = t.stride;
   a.plan_step = t.plan_step;
+  a.plan_pending = t.plan_pending;
+  a.plan_n_steps = t.plan_n_steps;
   if (t.bounds) std::copy(t.bounds, t.bounds + t.splits + 1, a.split_begin);
   const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
@@ -821,7 +828,12 @@ hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const f
     m.group = group;
     m.rows = rows;
     m.n_splits = t.splits;
+    m.advance = t.advance;
+    m.advance_cap = t.plan_n_steps;
     st = post_launch(ctx, hw::launch_merge(g.head_dim, m, s), "lse_merge", s);
+    if (st != HW_OK) return st;
+  } else if (t.advance) {
+    st = post_launch(ctx, hw::launch_advance(t.advance, t.plan_n_steps, s), "advance", s);
     if (st != HW_OK) return st;
   }
   return HW_OK;
@@ -841,8 +853,14 @@ hw_status decode_planned(hw_ctx *ctx, int32_t layer, int32_t n_new, const float 
   t.stride = 4;
   t.splits = p.splits;
   t.bounds = p.splits <= hw::kMaxBoundSplits ? p.bounds.data() : nullptr;
-  t.plan_step = reinterpret_cast<const int32_t *>(base + ctx->plan_cnt) + layer;
-  return launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
+  int32_t *counter = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + layer;
+  t.plan_step = counter;
+  t.plan_n_steps = p.n_steps;
+  t.plan_pending = p.pending[layer];
+  t.advance = p.pending[layer] ? counter : nullptr;
+  hw_status st = launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
+  if (st == HW_OK) ctx->plan.pending[layer] = 0;
+  return st;
 }
 
 // One decode of n_new query tokens per worker (n_new = 1: the one-token step), with its split
@@ -1095,7 +1113,9 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
     grow[b] = (int64_t)n_steps * tokens_per_step[i];
     rows += tokens_per_step[i];
   }
-  if (rows > (1 << 20)) return ctx->fail(HW_ERR_INVALID_ARG, "too many tokens per step");
+  if (rows > hw::kMaxPlanRows)
+    return ctx->fail(HW_ERR_INVALID_ARG, "a planned step takes at most " + std::to_string(hw::kMaxPlanRows) +
+                                             " tokens over all blocks");
   if (n_blocks > hw::kMaxPlanBlocks)
     return ctx->fail(HW_ERR_INVALID_ARG, "a plan takes at most " + std::to_string(hw::kMaxPlanBlocks) + " blocks");
   // Every block of the views and of the plan must have the same length in every layer: one
@@ -1257,6 +1277,7 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   p.bounds = std::move(bounds);
   p.append_blocks = std::move(ablk);
   p.append_pages = std::move(apages);
+  p.pending.assign((size_t)g.n_layers, 0);
   ctx->uploaded_valid = false;
   return HW_OK;
 }
@@ -1267,6 +1288,8 @@ hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *
   const Plan &p = ctx->plan;
   if (!p.active) return ctx->fail(HW_ERR_INVALID_ARG, "no step plan is active");
   if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (p.pending[layer])
+    return ctx->fail(HW_ERR_INVALID_ARG, "this layer's planned step is appended but not decoded yet");
   if (p.rows > 0 && (!k || !v)) return ctx->fail(HW_ERR_INVALID_ARG, "k/v NULL");
   if (((uintptr_t)k | (uintptr_t)v) % 16) return ctx->fail(HW_ERR_INVALID_ARG, "k/v must be 16-byte aligned");
   char *base = (char *)ctx->ws + ctx->off_plan;
@@ -1279,7 +1302,7 @@ hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *
   a.trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
   std::copy(p.append_blocks.begin(), p.append_blocks.end(), a.blocks);
   std::copy(p.append_pages.begin(), p.append_pages.end(), a.pages);
-  a.step = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + layer;
+  a.step = reinterpret_cast<const int32_t *>(base + ctx->plan_cnt) + layer;
   a.overflow = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + g.n_layers;
   a.n_blocks = (int32_t)p.blocks.size();
   a.rows = p.rows;
@@ -1288,7 +1311,12 @@ hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *
   a.page_size = g.page_size;
   a.page_groups = g.page_size / hw::kTokGroup;
   hipStream_t s = (hipStream_t)stream;
-  return post_launch(ctx, hw::launch_plan_append(g.kv_dtype, g.head_dim, a, s), "plan_append", s);
+  if (p.rows > 0) {   // (no planned token: nothing to write, the step still counts)
+    hw_status st = post_launch(ctx, hw::launch_plan_append(g.kv_dtype, g.head_dim, a, s), "plan_append", s);
+    if (st != HW_OK) return st;
+  }
+  ctx->plan.pending[layer] = 1;
+  return HW_OK;
 }
 
 hw_status hw_plan_end(hw_ctx *ctx, void *stream) {
@@ -1307,7 +1335,7 @@ hw_status hw_plan_end(hw_ctx *ctx, void *stream) {
   for (size_t i = 0; i < p.blocks.size(); ++i) {
     BlockState &bs = ctx->blocks[p.blocks[i]];
     for (int32_t l = 0; l < g.n_layers; ++l)
-      bs.len[l] = p.base[i] + std::min(cnt[l], p.n_steps) * p.tps[i];
+      bs.len[l] = p.base[i] + std::min(cnt[l] + p.pending[l], p.n_steps) * p.tps[i];
     const size_t keep = (size_t)((bs.max_len() + g.page_size - 1) / g.page_size);
     while (bs.pages.size() > keep) {
       ctx->free_stack.push_back(bs.pages.back());

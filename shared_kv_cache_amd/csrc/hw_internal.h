@@ -89,8 +89,12 @@ struct DecodeArgs {
   float *part_o;           // [n_splits][n_kv_heads][rows][head_dim] normalised partial outputs
   float *part_lse;         // [n_splits][n_kv_heads][rows] log2-domain partial normalisers
   // Step plan: the layer's counter of planned appends (null: no plan). Descriptors are then
-  // {x, segment << 8, v0, rate} and delta holds {d0, rate} pairs (see the kernel).
+  // {x, segment << 8, v0, rate} and delta holds {d0, rate} pairs (see the kernel). The
+  // decode sees min(counter + plan_pending, plan_n_steps) steps: plan_pending is 1 when this
+  // step's append was enqueued before the decode (the counter advances after the decode).
   const int32_t *plan_step;
+  int32_t plan_pending;
+  int32_t plan_n_steps;
   // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];
@@ -101,11 +105,14 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
 
 // The append of one planned step of one layer (a step plan, hw_plan_steps): every planned
 // block b takes its tokens_per_step tokens at local positions base(b) + s * tps(b) + j, s
-// being the layer's counter of planned appends, which the kernel then advances. The
-// planned blocks and the ids of the pages the window writes ride in the launch arguments,
-// so that the only dependent loads are the counter and the rope table's rows.
+// being the layer's counter of planned appends. The counter is NOT advanced here (every
+// workgroup reads it): the kernel that follows the layer's decode advances it (the merge,
+// or advance_kernel). The planned blocks and the ids of the pages the window writes ride in
+// the launch arguments, so that the only dependent loads are the counter and the rope
+// table's rows.
 constexpr int kMaxPlanBlocks = 64;
 constexpr int kMaxPlanPages = 512;
+constexpr int kMaxPlanRows = 1024;   // tokens per planned step, all blocks
 struct PlanBlock {
   int32_t base;       // length when the plan began
   int32_t tps;        // tokens per step
@@ -119,7 +126,7 @@ struct PlanAppendArgs {
   const void *k_src;       // [rows][n_kv_heads][head_dim], rows in planned-block order
   const void *v_src;
   const float2 *trig;      // [max_position][head_dim/2] (cos, sin)
-  int32_t *step;           // the layer's counter of planned appends
+  const int32_t *step;     // the layer's counter of planned appends
   int32_t *overflow;       // set to 1 by an append past the plan's last step (dropped)
   int32_t n_blocks;
   int32_t rows;            // tokens per step, all planned blocks
@@ -142,7 +149,15 @@ struct MergeArgs {
   int32_t group;
   int32_t rows;
   int32_t n_splits;
+  // Step plan: a layer counter to advance (by one, up to advance_cap) once the decode before
+  // this merge has read it; null: none.
+  int32_t *advance;
+  int32_t advance_cap;
 };
+
+// Advance a step plan's layer counter by one (up to cap): one thread, for decodes that
+// write their output directly (no merge follows them).
+hipError_t launch_advance(int32_t *counter, int32_t cap, hipStream_t s);
 
 hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
 

@@ -149,13 +149,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// plan_append: the append of one planned step of one layer, in ONE workgroup. Every thread
-// reads the layer's step counter s first; after a barrier, thread 0 advances it, so no
-// thread can see the advanced value. One item = (row, KV head, 8-dim chunk): the key's 8
-// rotated pairs (dims c, c + D/2 for c in the chunk) and the same 16 dims of the value.
+// plan_append: the append of one planned step of one layer; one workgroup per input row.
+// Every thread reads the layer's step counter s and nothing here writes it (the kernel
+// after the layer's decode advances it). Values: one element per thread and pass, the
+// passes' loads issued before their stores. Keys: one item = (KV head, 8-dim chunk), the 8
+// rotated pairs (dims c, c + D/2 for c in the chunk), written 16 bytes at a time.
 // ------------------------------------------------------------------------------------
 template <typename KV, int D>
-__global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
+__global__ __launch_bounds__(256) void plan_append_kernel(PlanAppendArgs a) {
   constexpr int kChunks = D / 16;
   constexpr int kVec = 16 / (int)sizeof(KV);   // elements per 16-byte access
   static_assert(8 % kVec == 0, "8-element chunks in 16-byte accesses");
@@ -166,40 +167,53 @@ __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
   KV *__restrict__ vdst = static_cast<KV *>(a.v_layer);
   const int s = a.step[0];
   if (s >= a.n_steps) {   // past the plan: nothing is written, the host reports it
-    if (threadIdx.x == 0) a.overflow[0] = 1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.overflow[0] = 1;
     return;
   }
-  const int items = a.rows * hkv * kChunks;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int c8 = it % kChunks;
-    const int h = (it / kChunks) % hkv;
-    const int r = it / (kChunks * hkv);
-    int bi = 0;
-    for (int i = 0; i < a.n_blocks; ++i)
-      if (r >= a.blocks[i].row0 && r < a.blocks[i].row0 + a.blocks[i].tps) bi = i;
-    const PlanBlock &b = a.blocks[bi];
-    const int pos = b.base + s * b.tps + (r - b.row0);
-    const int page = a.pages[b.pages_off + pos / a.page_size - b.page0];
-    const int t = pos % a.page_size;
-    // Every load of the item, 16 bytes at a time, before any use: the 8 dims of the chunk
-    // in each half of the head for K and V, and the chunk's 8 (cos, sin) pairs.
-    const size_t src = ((size_t)r * hkv + h) * D;
-    uint4 kl[8 / kVec], kh[8 / kVec], vl[8 / kVec], vh[8 / kVec];
+  // This workgroup's row: its block (wave-uniform search), position, page and slot.
+  const int r = blockIdx.x;
+  int bi = 0;
+  for (int i = 0; i < a.n_blocks; ++i)
+    if (r >= a.blocks[i].row0 && r < a.blocks[i].row0 + a.blocks[i].tps) bi = i;
+  const PlanBlock &b = a.blocks[bi];
+  const int pos = b.base + s * b.tps + (r - b.row0);
+  const int page = a.pages[b.pages_off + pos / a.page_size - b.page0];
+  const int t = pos % a.page_size, u = t & 31;
+  const size_t head0 = (size_t)page * hkv * a.page_groups + t / 32;   // group of KV head 0
+  const size_t src0 = (size_t)r * hkv * D;
+  // Values: thread -> (head, dim), consecutive threads on consecutive dims.
+  constexpr int VU = 4;
+  for (int i0 = threadIdx.x; i0 < hkv * D; i0 += blockDim.x * VU) {
+    KV val[VU];
+#pragma unroll
+    for (int k = 0; k < VU; ++k) {
+      const int idx = i0 + k * blockDim.x;
+      val[k] = vsrc[src0 + (idx < hkv * D ? idx : 0)];
+    }
+#pragma unroll
+    for (int k = 0; k < VU; ++k) {
+      const int idx = i0 + k * blockDim.x;
+      if (idx < hkv * D) {
+        const int h = idx / D, i = idx % D;
+        vdst[(head0 + (size_t)h * a.page_groups) * (size_t)(32 * D) + v_index(u, i)] = val[k];
+      }
+    }
+  }
+  // Keys: thread -> (head, 8-dim chunk).
+  for (int it = threadIdx.x; it < hkv * kChunks; it += blockDim.x) {
+    const int c8 = it % kChunks, h = it / kChunks;
+    const size_t src = src0 + (size_t)h * D;
+    uint4 kl[8 / kVec], kh[8 / kVec];
 #pragma unroll
     for (int j = 0; j < 8 / kVec; ++j) {
       kl[j] = *reinterpret_cast<const uint4 *>(ksrc + src + 8 * c8 + kVec * j);
       kh[j] = *reinterpret_cast<const uint4 *>(ksrc + src + D / 2 + 8 * c8 + kVec * j);
-      vl[j] = *reinterpret_cast<const uint4 *>(vsrc + src + 8 * c8 + kVec * j);
-      vh[j] = *reinterpret_cast<const uint4 *>(vsrc + src + D / 2 + 8 * c8 + kVec * j);
     }
     float4 cs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       cs[j] = reinterpret_cast<const float4 *>(a.trig + (size_t)pos * (D / 2) + 8 * c8)[j];
-    const size_t grp = ((size_t)page * hkv + h) * a.page_groups + t / 32;
-    const int u = t & 31;
     const KV *x0 = reinterpret_cast<const KV *>(kl), *x1 = reinterpret_cast<const KV *>(kh);
-    const KV *w0 = reinterpret_cast<const KV *>(vl), *w1 = reinterpret_cast<const KV *>(vh);
     const float *cf = reinterpret_cast<const float *>(cs);
     float lo[8], hi[8];
 #pragma unroll
@@ -214,8 +228,8 @@ __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
       }
       rotate_pair(a0, a1, cf[2 * e], cf[2 * e + 1], lo[e], hi[e]);
     }
-    // Keys: the chunk's 8 dims of one token are contiguous in the K layout (16 or 32 bytes).
-    KV *kg = kdst + grp * (size_t)(32 * D);
+    // The chunk's 8 dims of one token are contiguous in the K layout (16 or 32 bytes).
+    KV *kg = kdst + (head0 + (size_t)h * a.page_groups) * (size_t)(32 * D);
     KV *klo = kg + k_index(u, 8 * c8), *khi = kg + k_index(u, D / 2 + 8 * c8);
     if constexpr (sizeof(KV) == 2) {
       uint4 wlo, whi;
@@ -235,16 +249,16 @@ __global__ __launch_bounds__(1024) void plan_append_kernel(PlanAppendArgs a) {
       reinterpret_cast<float4 *>(khi)[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
       reinterpret_cast<float4 *>(khi)[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
     }
-    // Values: one element per dim (the V layout keeps 8 tokens of a dim together).
-    KV *vg = vdst + grp * (size_t)(32 * D);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      vg[v_index(u, 8 * c8 + e)] = w0[e];
-      vg[v_index(u, D / 2 + 8 * c8 + e)] = w1[e];
-    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) a.step[0] = s + 1;
+}
+
+// One thread: a step plan's layer counter, advanced by one up to cap (the decode of the
+// layer has read it). Used when no merge follows the decode.
+__global__ void advance_kernel(int32_t *counter, int32_t cap) {
+  if (threadIdx.x == 0) {
+    const int v = counter[0];
+    counter[0] = v < cap ? v + 1 : v;
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -784,7 +798,10 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // unconditionally keep the waits for each stage exact.
   // Step plan: planned appends of this layer so far (wave-uniform, scalar cache).
   int pstep = 0;
-  if constexpr (PLAN) pstep = *(const ConstInt *)a.plan_step;
+  if constexpr (PLAN) {
+    const int c = *(const ConstInt *)a.plan_step + a.plan_pending;
+    pstep = c < a.plan_n_steps ? c : a.plan_n_steps;
+  }
   int s_lo = 0, s_hi = -1;
   if (COOP && end > begin) {
     s_lo = load_desc<MT>(hd.groups, begin, hd.desc_stride).y >> 8;
@@ -1284,6 +1301,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     acc = acc * fs + oa * fo;
     mm = nm;
   }
+  if (a.advance && blockIdx.x == 0 && threadIdx.x == 0) {   // the decode has read the counter
+    const int v = a.advance[0];
+    a.advance[0] = v < a.advance_cap ? v + 1 : v;
+  }
   if (!live || sub != 0) return;
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   reinterpret_cast<float4 *>(a.out + ((size_t)w * a.n_q_heads + h) * D)[q4] =
@@ -1323,8 +1344,13 @@ hipError_t launch_append(hw_dtype dt, int head_dim, const AppendArgs &a, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_advance(int32_t *counter, int32_t cap, hipStream_t s) {
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, counter, cap);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan_append(hw_dtype dt, int head_dim, const PlanAppendArgs &a, hipStream_t s) {
-  dim3 grid(1), block(1024);
+  dim3 grid(a.rows > 0 ? a.rows : 1), block(256);
   if (dt == HW_BF16) {
     if (head_dim == 128)
       hipLaunchKernelGGL((plan_append_kernel<__bf16, 128>), grid, block, 0, s, a);

@@ -205,3 +205,38 @@ def test_w8_32k_step_graph_replays_equal_eager_and_the_oracle():
             assert ca.block_info(b, layer)[0] == wl.lengths[b] + 3
     ca.close()
     cb.close()
+
+
+def test_plan_step_order_rules():
+    # A layer's planned step is append, then decode; the decode's kernels advance the
+    # layer's count. A second append before the decode is refused; a decode without an
+    # append sees the state as it is (bitwise the same output twice); a step appended but
+    # not decoded when the plan ends still counts.
+    wl = _small_workload(1)
+    cache = make_cache(wl, max_splits=64)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    cache.plan_steps(3, wl.inprogress, [1, 1, 1, 1])
+    rng = np.random.default_rng(9)
+
+    def kv():
+        return [kv_tensor(W.round_to_bf16_values(rng.standard_normal((4, 8, 128), dtype=np.float32)),
+                          "bf16") for _ in range(2)]
+
+    q = wl.q(0, 1)
+    cache.append_step(0, *kv())
+    with pytest.raises(H.HwError) as e:
+        cache.append_step(0, *kv())
+    assert e.value.status == H.HW_ERR_INVALID_ARG
+    a1 = decode_np(cache, 0, q)
+    a2 = decode_np(cache, 0, q)          # no append in between: same state, same bits
+    np.testing.assert_array_equal(a1[0], a2[0])
+    np.testing.assert_array_equal(a1[1], a2[1])
+    cache.append_step(0, *kv())
+    decode_np(cache, 0, q)
+    cache.append_step(0, *kv())          # third step appended, never decoded
+    torch.cuda.synchronize()
+    cache.plan_end()
+    for b in wl.inprogress:
+        assert cache.block_info(b, 0)[0] == wl.lengths[b] + 3
+    cache.close()
