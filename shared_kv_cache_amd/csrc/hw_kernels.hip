@@ -304,17 +304,20 @@ struct Frag<__bf16, D> {
     for (int dt = 0; dt < NDT; ++dt) v[dt] = ld16<NT>(vg + (dt * 64 + lane) * 8);
   }
   // The same 16 loads straight into LDS (one 1 KiB slot per load, lane l's 16 bytes at
-  // l * 16), streaming hint; stage_read then picks up exactly what load would have given.
+  // l * 16), with the streaming hint when NT; stage_read then picks up exactly what load
+  // would have given.
+  template <bool NT = true>
   __device__ __forceinline__ static void load_lds(const __bf16 *kg, const __bf16 *vg, int lane,
                                                   uint4 (*slot)[64]) {
+    constexpr int aux = NT ? 2 : 0;   // cache policy: nt
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        __builtin_amdgcn_global_load_lds(kg + ((c * 2 + hh) * 64 + lane) * 8, &slot[c * 2 + hh][0], 16, 0, 2);
+        __builtin_amdgcn_global_load_lds(kg + ((c * 2 + hh) * 64 + lane) * 8, &slot[c * 2 + hh][0], 16, 0, aux);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-      __builtin_amdgcn_global_load_lds(vg + (dt * 64 + lane) * 8, &slot[NC * 2 + dt][0], 16, 0, 2);
+      __builtin_amdgcn_global_load_lds(vg + (dt * 64 + lane) * 8, &slot[NC * 2 + dt][0], 16, 0, aux);
   }
   __device__ __forceinline__ void stage_read(const uint4 (*slot)[64], int lane) {
 #pragma unroll
@@ -517,15 +520,17 @@ struct Stage {
   int desc_x, desc_y, desc_ls;
 };
 
-// Issue one group's K and V loads (each group is read by one wave: streaming hint).
-template <typename KV, int D>
+// Issue one group's K and V loads. NTH: the group is read by one wave only (streaming
+// hint). Several row blocks of one KV head read every group once each (several query
+// tokens per worker): their loads are ordinary, so that all but the first read hit L2.
+template <typename KV, int D, bool NTH = true>
 __device__ __forceinline__ void fetch_group(Stage<KV, D> &st, GDesc desc, const KV *kl,
                                             const KV *vl, size_t head_groups, int lane) {
   st.desc_x = desc.x;
   st.desc_y = desc.y;
   st.desc_ls = desc.ls;
   const size_t gb = ((size_t)desc.x + head_groups) * (size_t)(32 * D);
-  st.f.template load<true>(kl + gb, vl + gb, lane);
+  st.f.template load<NTH>(kl + gb, vl + gb, lane);
 }
 
 // The query offset of worker w for the block of segment seg. Under a step plan the table
@@ -676,7 +681,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   constexpr int QSTRIDE = D + 4;                    // padded q row (LDS bank spread)
   constexpr int Q_FLOATS = RT * 16 * QSTRIDE;
   // Rotated query operands: per phase segment (COOP) or per wave, [rt][chunk][lane] each.
-  constexpr bool LDSST = WIDE && std::is_same<KV, __bf16>::value;   // LDS stage, see above
+  constexpr bool LDSST = NST == 1 && std::is_same<KV, __bf16>::value;   // LDS stage, see above
   constexpr int NLOAD = NC * 2 + NDT;               // 16-byte loads per lane per group
   constexpr int QT_FLOATS = LDSST ? 0 : (COOP ? CAP : NW) * RT * NC * 64 * (int)(sizeof(QOp) / 4);
   constexpr int STAGE_FLOATS = LDSST ? NW * NLOAD * 64 * 4 : 0;
@@ -860,9 +865,16 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     fetch_group(st, desc, kl, vl, head_groups, lane);
     wide_rows(dl_cur, ow);
+  } else if constexpr (LDSST) {
+    // narrow descriptors: the offsets of groups 0 and 1 are vector loads, in before group 0
+    // is requested, as the queries are
+    fetch_delta<PLAN>(dl_cur, desc.y >> 8, a, row_w, pstep);
+    fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    fetch_group<KV, D, !MT>(st, desc, kl, vl, head_groups, lane);
   } else {
     fetch_delta<PLAN>(dl_cur, desc.y >> 8, a, row_w, pstep);
-    fetch_group(st, desc, kl, vl, head_groups, lane);
+    fetch_group<KV, D, !MT>(st, desc, kl, vl, head_groups, lane);
     fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
   }
   // Stage the queries, pre-scaled by softmax_scale * log2(e), the offsets and the rotation
@@ -1100,7 +1112,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     __builtin_amdgcn_s_setprio(1);
     if (wcount > 1) {
       const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
-      F::load_lds(kl + gb, vl + gb, lane, stage);
+      F::template load_lds<!MT>(kl + gb, vl + gb, lane, stage);
     }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -1115,15 +1127,22 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       st.desc_ls = next.ls;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage read before it is refilled
       next = next2;                                         // group i + 1
-      ow = ow_next;
-      ow_next = ow_next2;
-      wide_rows(dl_cur, ow);                                // group i's offsets
+      if constexpr (WIDE) {
+        ow = ow_next;
+        ow_next = ow_next2;
+        wide_rows(dl_cur, ow);                              // group i's offsets
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) dl_cur[rt] = dl_next[rt];   // loaded with group i
+      }
       enter(st, 0, dl_cur);
       __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < wcount) {
         const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
-        F::load_lds(kl + gb, vl + gb, lane, stage);
+        F::template load_lds<!MT>(kl + gb, vl + gb, lane, stage);
       }
+      // narrow descriptors: group i + 1's offsets, in when its fill is
+      if constexpr (!WIDE) fetch_delta<PLAN>(dl_next, next.y >> 8, a, row_w, pstep);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       next2 = desc_at(min(wfirst + i + 2, wlast), ow_next2);
@@ -1136,7 +1155,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
       if (i > 0) {
         desc = next;
         next = next2;
-        fetch_group(st, desc, kl, vl, head_groups, lane);
+        fetch_group<KV, D, !MT>(st, desc, kl, vl, head_groups, lane);
         if constexpr (WIDE) {
           ow = ow_next;
           ow_next = ow_next2;
