@@ -3,9 +3,10 @@
 
 A step is one decode step of every worker over every layer the workload times
 (for w8_32k each layer first appends one new token per worker: under a step
-plan by default, hw_append_step + hw_concurrent_decode, optionally replayed as
-one HIP graph). Inputs are seeded synthetic tensors already resident in HBM
-when a timed region starts. With --query-tokens K > 1 every worker queries K
+plan by default, hw_append_step + hw_concurrent_decode). The step is captured
+once as a HIP graph and replayed, as a serving loop runs its decode step
+(--eager: every kernel launched from the host). Inputs are seeded synthetic
+tensors already resident in HBM when a timed region starts. With --query-tokens K > 1 every worker queries K
 tokens per step together (hw_concurrent_decode_tokens, causal).
 
 Prints ONE JSON line. The headline workload (default w4_16k) gives `value`
@@ -316,6 +317,25 @@ def _oracle_layer(job):
         return layer, time.perf_counter() - t0
 
 
+def cpu_description():
+    """The first processor's identification in /proc/cpuinfo: its model name as the kernel
+    reports it (virtual machines may give only a family name), with vendor, family, model
+    and stepping numbers."""
+    fields = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if not ln.strip():
+                    break                       # end of the first processor's entry
+                k, _, v = ln.partition(":")
+                fields.setdefault(k.strip(), v.strip())
+    except OSError:
+        return "unknown"
+    ident = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping")
+                      if k in fields)
+    return f"{fields.get('model name', 'unknown')} ({ident})" if ident else fields.get("model name", "unknown")
+
+
 def cpu_baseline_child(name, layout, kq, procs):
     """Runs in a child process that never touches the GPU: the fp64 oracle, as it stands, on
     one full step of the workload (every layer, worker and query head), layer l on pool
@@ -327,12 +347,7 @@ def cpu_baseline_child(name, layout, kq, procs):
 
     wl = W.make(name)
     L = wl.n_layers
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
-    except OSError:
-        pass
+    model = cpu_description()
     one = _oracle_layer((name, 0, layout, kq, L))[1]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -395,8 +410,10 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="layer pools to rotate through (0: the workload's own count; 1 keeps one "
                          "layer's K/V resident in the last-level cache)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of the whole step captured as one HIP graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step's kernels from the host instead of replaying the "
+                         "step captured once as a HIP graph (the default)")
+    ap.add_argument("--graph", action="store_true", help=argparse.SUPPRESS)   # the default
     ap.add_argument("--no-plan", action="store_true",
                     help="growing workloads: host-planned appends (hw_append_kv) instead of a step plan")
     ap.add_argument("--query-tokens", type=int, default=1,
@@ -431,15 +448,18 @@ def main() -> int:
         log("copy calibration: 3 x torch.mul(src, 1.0, out=dst), 1 GiB read + 1 GiB written each")
 
     plan = not args.no_plan
-    head = run_gpu(args.workload, args, args.graph, plan)
+    def graphed(name):
+        # a growing workload replays a captured step only under a step plan (one token)
+        grows = name == "w8_32k"
+        return not args.eager and (not grows or (plan and args.query_tokens == 1))
+
+    head = run_gpu(args.workload, args, graphed(args.workload), plan)
     log(f"{args.workload}: median {head['ms_step']:.4f} ms/step over {args.repeats} x "
         f"{args.steps} steps; decode kernel {head['dec_avg_ms'] * 1e3:.2f} us")
     extra = None
     if args.extra_workload != "none" and args.extra_workload != args.workload:
-        # the second workload in its own best configuration: growing ones under a step plan,
-        # replayed as one HIP graph
-        grows = args.extra_workload == "w8_32k"
-        extra = run_gpu(args.extra_workload, args, grows and plan, plan)
+        # the second workload the same way: growing ones under a step plan
+        extra = run_gpu(args.extra_workload, args, graphed(args.extra_workload), plan)
         log(f"{args.extra_workload}: median {extra['ms_step']:.4f} ms/step; decode kernel "
             f"{extra['dec_avg_ms'] * 1e3:.2f} us")
     stream_read = stream_ceiling([int(head["launch_bytes"]), 512 << 20])

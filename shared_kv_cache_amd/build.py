@@ -32,7 +32,8 @@ FLAGS = [
 ]
 
 
-ASAN_HOST = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_HOST = ["-O1", "-g", "-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def build(verbose: bool = True, out: str = LIB, extra=()) -> str:

@@ -210,7 +210,12 @@ hw_status check_config(const hw_config *g, std::string &m) {
     return m = "max_workers * max_query_tokens * n_q_heads * head_dim must be below 2^31",
            HW_ERR_INVALID_ARG;
   if (g->max_splits < 0 || g->max_splits > 65535) return m = "max_splits out of range", HW_ERR_INVALID_ARG;
-  if (g->kv_dtype != HW_BF16 && g->kv_dtype != HW_F32) return m = "unknown kv_dtype", HW_ERR_INVALID_ARG;
+  // The caller's bytes are read as an integer: loading a value outside the enum's range
+  // through the enum type would itself be undefined behaviour.
+  int32_t dtype_raw;
+  static_assert(sizeof(g->kv_dtype) == sizeof(dtype_raw), "hw_dtype is stored as a 32-bit int");
+  std::memcpy(&dtype_raw, &g->kv_dtype, sizeof dtype_raw);
+  if (dtype_raw != HW_BF16 && dtype_raw != HW_F32) return m = "unknown kv_dtype", HW_ERR_INVALID_ARG;
   if (!(g->rope_theta > 1.0) || !std::isfinite(g->rope_theta)) return m = "rope_theta must be > 1", HW_ERR_INVALID_ARG;
   if (!(g->softmax_scale >= 0.0f) || !std::isfinite(g->softmax_scale))
     return m = "softmax_scale must be finite and >= 0", HW_ERR_INVALID_ARG;

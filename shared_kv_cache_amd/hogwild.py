@@ -6,7 +6,9 @@ convenience owner that allocates the pools and the workspace as torch device
 tensors (PyTorch supplies device memory and streams, nothing else).
 
 There is no fallback: if ``_lib/libhogwild.so`` is missing, importing this
-module's functions raises ``ImportError`` telling how to build it.
+module's functions raises ``ImportError`` telling how to build it. The environment
+variable ``HOGWILD_LIBRARY`` names another build of the same library to load instead
+(for instance the sanitizer build of ``build.py --asan-host``).
 """
 
 from __future__ import annotations
@@ -16,7 +18,8 @@ import os
 from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 from typing import Optional, Sequence
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libhogwild.so")
+LIB_PATH = os.environ.get("HOGWILD_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "_lib", "libhogwild.so")
 
 HW_OK, HW_ERR_INVALID_ARG, HW_ERR_OUT_OF_PAGES, HW_ERR_STALE_VIEW, HW_ERR_WORKSPACE, HW_ERR_HIP = range(6)
 HW_BF16, HW_F32 = 0, 1
