@@ -3,9 +3,9 @@
 
 A step is one decode step of every worker over every layer the workload times
 (for w8_32k each layer first appends one new token per worker: under a step
-plan by default, hw_append_step + hw_concurrent_decode). The step is captured
-once as a HIP graph and replayed, as a serving loop runs its decode step
-(--eager: every kernel launched from the host). Inputs are seeded synthetic
+plan by default, hw_append_step + hw_concurrent_decode). A step of at least 8
+layers is captured once as a HIP graph and replayed, as a serving loop runs its
+decode step (--eager: every kernel launched from the host). Inputs are seeded synthetic
 tensors already resident in HBM when a timed region starts. With --query-tokens K > 1 every worker queries K
 tokens per step together (hw_concurrent_decode_tokens, causal).
 
@@ -449,9 +449,13 @@ def main() -> int:
 
     plan = not args.no_plan
     def graphed(name):
-        # a growing workload replays a captured step only under a step plan (one token)
+        # A step of a few layers launches faster than a graph replays (tiny_fp32, one decode
+        # launch: 9.3 us eager, 18 us replayed), so only steps of at least 8 layers are
+        # replayed. A growing workload replays a captured step only under a step plan.
+        from shared_kv_cache_amd import workloads as W
         grows = name == "w8_32k"
-        return not args.eager and (not grows or (plan and args.query_tokens == 1))
+        many = (args.layers or W.make(name).n_layers) >= 8
+        return not args.eager and many and (not grows or (plan and args.query_tokens == 1))
 
     head = run_gpu(args.workload, args, graphed(args.workload), plan)
     log(f"{args.workload}: median {head['ms_step']:.4f} ms/step over {args.repeats} x "
