@@ -125,6 +125,26 @@ def test_w2_4k_parity_and_split_invariance():
     cache.close()
 
 
+def test_fp32_results_across_partition_counts():
+    # fp32 pools keep fp32 probabilities: the partition count changes only the order of fp32
+    # sums, so 1 and 5 partitions agree to fp32 rounding (the bf16 bound above comes from
+    # bf16 probabilities rounded against each partition's own running maximum).
+    wl = W.make("tiny_fp32")
+    cache = make_cache(wl)
+    fill_layer(cache, wl, 0)
+    cache.set_views(wl.views())
+    q = wl.q(0)
+    H.hw_set_split(cache.ctx, 1)
+    o1, l1 = decode_np(cache, 0, q)
+    H.hw_set_split(cache.ctx, 5)
+    o5, l5 = decode_np(cache, 0, q)
+    H.hw_set_split(cache.ctx, 0)
+    _say(f"fp32 split 1 vs 5: {rel_l2(o5, o1):.3e}, lse {np.max(np.abs(l5 - l1)):.3e}")
+    assert rel_l2(o5, o1) <= TOL["f32"]
+    assert np.max(np.abs(l5 - l1)) <= TOL["f32"]
+    cache.close()
+
+
 def test_page_scatter_invariance_is_bitwise():
     wl = W.make("w2_4k", n_layers=1)
     outs = []
