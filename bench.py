@@ -82,6 +82,7 @@ def run_gpu(name, args, graph, plan):
     kq = args.query_tokens
     grows = name == "w8_32k"
     plan = plan and grows and kq == 1
+    fused = plan and not getattr(args, "unfused", False)
     steps, reps = args.steps, args.repeats
     # planned window: warm-up, the timed repeats, the kernel-event pass, graph warm-up
     total_steps = args.warmup + reps * steps + steps + 4
@@ -135,6 +136,11 @@ def run_gpu(name, args, graph, plan):
         for layer in range(L):
             if grows:
                 k, v = step_kv[layer]
+                if plan and fused:   # the append runs inside the decode launch
+                    H.hw_decode_step(cache.ctx, layer, k.data_ptr(), v.data_ptr(),
+                                     q_dev[layer].data_ptr(), outs[layer].data_ptr(),
+                                     lses[layer].data_ptr(), stream)
+                    continue
                 if plan:
                     H.hw_append_step(cache.ctx, layer, k.data_ptr(), v.data_ptr(), stream)
                 else:
@@ -221,7 +227,7 @@ def run_gpu(name, args, graph, plan):
     step_bytes = L * (launch_bytes + append_bytes)
     dec_avg = float(np.mean(dec_ms))
     return {
-        "wl": wl, "plan": plan, "graph": graph, "ms_step": med,
+        "wl": wl, "plan": plan, "fused": fused, "graph": graph, "ms_step": med,
         "spread": {"repeats": reps, "steps_per_repeat": steps,
                    "ms_per_step_min": round(min(ms) / steps, 5),
                    "ms_per_step_p10": round(pct(ms, 0.1) / steps, 5),
@@ -252,6 +258,7 @@ def describe(r, args, layout):
         "per_layer_other_us": round(r["ms_step"] * 1e3 / wl.n_layers - r["dec_avg_ms"] * 1e3, 3),
         "appends_per_step": wl.n_layers if wl.name == "w8_32k" else 0,
         "query_tokens": args.query_tokens, "hip_graph": r["graph"], "step_plan": r["plan"],
+        "append_fused_into_decode": r["fused"],
     }
     roofline = {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4),
@@ -416,6 +423,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true", help=argparse.SUPPRESS)   # the default
     ap.add_argument("--no-plan", action="store_true",
                     help="growing workloads: host-planned appends (hw_append_kv) instead of a step plan")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step plans: append (hw_append_step) and decode as two calls instead of "
+                         "hw_decode_step, the append fused into the decode")
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="query tokens per worker and step (several: one causal decode of all)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)

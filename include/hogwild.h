@@ -260,6 +260,20 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
  * the layer before its decode), HW_ERR_HIP. */
 hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, void *stream);
 
+/* One planned step of one layer with its append fused into the decode (summary s8: the
+ * step's tokens are appended, then attended): the same results, pool bytes and counts as
+ * hw_append_step(layer, k, v) followed by hw_concurrent_decode(layer, q, out, lse), in one
+ * decode launch (plus the split merge) instead of two. Each (KV head, token group) is read by
+ * one wave of the decode; the wave whose groups the step's tokens fall in writes those tokens
+ * for its KV head before reading them, so no other synchronisation is needed. k, v as for
+ * hw_append_step; q, out, lse as for hw_concurrent_decode. Capturable (no host work).
+ * Errors: as hw_append_step and hw_concurrent_decode; HW_ERR_INVALID_ARG when the plan has a
+ * growing block that no view holds, or more query rows per KV head than one decode
+ * workgroup takes (64 for bf16): use the two calls then. A step past the window writes
+ * nothing and is reported by hw_plan_end. */
+hw_status hw_decode_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, const float *q,
+                         float *out, float *lse, void *stream);
+
 /* End the active plan: waits for `stream`, reads the device's per-layer counts of planned
  * steps back (a layer appended but not yet decoded counts its append), sets every planned
  * block's length in each layer to base + count * tokens_per_step, and returns the pages

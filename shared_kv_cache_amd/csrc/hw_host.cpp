@@ -79,6 +79,9 @@ struct Plan {
   std::vector<int32_t> bounds;              // partition bounds (splits <= kMaxBoundSplits)
   std::vector<hw::PlanBlock> append_blocks; // the planned append's launch arguments
   std::vector<int32_t> append_pages;
+  // hw_decode_step: every growing planned block is in some view (its groups are in the
+  // list, so some decode wave writes each of its tokens) and the decode has one row block
+  bool fusable = false;
   // per layer: 1 while the step's append is enqueued and its decode not yet (the layer's
   // counter advances after that decode)
   std::vector<uint8_t> pending;
@@ -101,9 +104,9 @@ struct hw_ctx {
   size_t ws_bytes = 0;
   size_t off_trig = 0, off_freq = 0, off_tables = 0, off_part_o = 0, off_part_lse = 0;
   size_t tables_bytes = 0;
-  // step-plan region: counters [n_layers] + overflow flag, {d0, rate} offsets, 4-int
-  // group descriptors
-  size_t off_plan = 0, plan_cnt = 0, plan_delta = 0, plan_groups = 0;
+  // step-plan region: counters [n_layers] + overflow flag, the fused step's per-block table,
+  // {d0, rate} offsets, 4-int group descriptors
+  size_t off_plan = 0, plan_cnt = 0, plan_fuse = 0, plan_delta = 0, plan_groups = 0;
   Plan plan;
   size_t part_o_bytes = 0, part_lse_bytes = 0, total_bytes = 0;
 
@@ -180,6 +183,8 @@ void layout_workspace(hw_ctx *c) {
   size_t po = 0;
   c->plan_cnt = po;
   po = align_up(po + ((size_t)g.n_layers + 1) * sizeof(int32_t));
+  c->plan_fuse = po;
+  po = align_up(po + (size_t)hw::kMaxPlanBlocks * 4 * sizeof(int32_t));
   c->plan_delta = po;
   po = align_up(po + (size_t)g.max_blocks * g.max_workers * 2 * sizeof(int32_t));
   c->plan_groups = po;
@@ -760,6 +765,11 @@ struct DecodeTables {
   const int32_t *plan_step = nullptr;   // step plans: the layer's counter of planned appends
   int32_t plan_pending = 0, plan_n_steps = 0;
   int32_t *advance = nullptr;           // counter to advance once the decode has read it
+  // hw_decode_step: the step's new keys and values, appended by the decode itself
+  const void *fuse_k = nullptr, *fuse_v = nullptr;
+  const int32_t *fuse_blocks = nullptr;
+  int32_t *fuse_overflow = nullptr;
+  int32_t fuse_n_blocks = 0;
 };
 
 // Split partials of a decode: the workspace's, or a caller-provided buffer of the same shape.
@@ -811,6 +821,12 @@ hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const f
   a.plan_step = t.plan_step;
   a.plan_pending = t.plan_pending;
   a.plan_n_steps = t.plan_n_steps;
+  a.fuse_k = t.fuse_k;
+  a.fuse_v = t.fuse_v;
+  a.fuse_trig = reinterpret_cast<const float2 *>((char *)ctx->ws + ctx->off_trig);
+  a.fuse_blocks = t.fuse_blocks;
+  a.fuse_overflow = t.fuse_overflow;
+  a.fuse_n_blocks = t.fuse_n_blocks;
   if (t.bounds) std::copy(t.bounds, t.bounds + t.splits + 1, a.split_begin);
   const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
@@ -844,9 +860,11 @@ hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const f
   return HW_OK;
 }
 
-// A decode under the active step plan: its tables were uploaded by hw_plan_steps.
+// A decode under the active step plan: its tables were uploaded by hw_plan_steps. With fuse_k
+// set (hw_decode_step) the decode also performs the layer's planned append of the step.
 hw_status decode_planned(hw_ctx *ctx, int32_t layer, int32_t n_new, const float *q, float *out,
-                         float *lse, hipStream_t s, Partials part) {
+                         float *lse, hipStream_t s, Partials part, const void *fuse_k = nullptr,
+                         const void *fuse_v = nullptr) {
   const Plan &p = ctx->plan;
   if (n_new != 1)
     return ctx->fail(HW_ERR_INVALID_ARG, "several query tokens per worker are not supported under a step plan");
@@ -863,6 +881,15 @@ hw_status decode_planned(hw_ctx *ctx, int32_t layer, int32_t n_new, const float 
   t.plan_n_steps = p.n_steps;
   t.plan_pending = p.pending[layer];
   t.advance = p.pending[layer] ? counter : nullptr;
+  if (fuse_k) {   // the step's append is this decode's: it sees one more step, then counts it
+    t.plan_pending = 1;
+    t.advance = counter;
+    t.fuse_k = fuse_k;
+    t.fuse_v = fuse_v;
+    t.fuse_blocks = reinterpret_cast<const int32_t *>(base + ctx->plan_fuse);
+    t.fuse_overflow = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + ctx->cfg.n_layers;
+    t.fuse_n_blocks = (int32_t)p.blocks.size();
+  }
   hw_status st = launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
   if (st == HW_OK) ctx->plan.pending[layer] = 0;
   return st;
@@ -1209,9 +1236,11 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   const int32_t gpp = g.page_size / hw::kTokGroup;
   std::vector<int32_t> gtab;
   std::vector<uint8_t> seg_first;
+  std::vector<int32_t> first_group(g.max_blocks, -1);   // list index of a block's group 0
   for (int32_t sg = 0; sg < n_seg; ++sg) {
     const int32_t b = seg_blocks[sg];
     const auto &pl = page_list(b);
+    first_group[b] = (int32_t)(gtab.size() / 4);
     for (int64_t t = 0; t < cap(b); t += hw::kTokGroup) {
       gtab.push_back(pl[t / g.page_size] * g.n_kv_heads * gpp + (int32_t)((t % g.page_size) / hw::kTokGroup));
       gtab.push_back(sg << 8);
@@ -1245,10 +1274,21 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   if (apages.size() > (size_t)hw::kMaxPlanPages)
     return ctx->fail(HW_ERR_INVALID_ARG, "the plan's window spans more than " +
                                              std::to_string(hw::kMaxPlanPages) + " pages");
+  // The fused step's table: per block {base length, tokens per step, first row, list index of
+  // its group 0 (-1: in no view)}.
+  std::vector<int32_t> ftab;
+  bool fusable = row_blocks_for(ctx, rows_q) == 1;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const hw::PlanBlock &pb = ablk[i];
+    const int32_t g0 = first_group[block_ids[i]];
+    ftab.insert(ftab.end(), {pb.base, pb.tps, pb.row0, g0});
+    if (pb.tps > 0 && g0 < 0) fusable = false;
+  }
   // One upload of the whole region, counters zeroed; the plan is set-up, not a step, so the
   // call waits for it.
   const size_t region = ctx->plan_groups + gtab.size() * sizeof(int32_t);
   std::vector<char> host(region, 0);
+  if (!ftab.empty()) std::memcpy(host.data() + ctx->plan_fuse, ftab.data(), ftab.size() * 4);
   if (!dtab.empty()) std::memcpy(host.data() + ctx->plan_delta, dtab.data(), dtab.size() * 4);
   if (!gtab.empty()) std::memcpy(host.data() + ctx->plan_groups, gtab.data(), gtab.size() * 4);
   hipStream_t s = (hipStream_t)stream;
@@ -1282,6 +1322,7 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   p.bounds = std::move(bounds);
   p.append_blocks = std::move(ablk);
   p.append_pages = std::move(apages);
+  p.fusable = fusable;
   p.pending.assign((size_t)g.n_layers, 0);
   ctx->uploaded_valid = false;
   return HW_OK;
@@ -1322,6 +1363,25 @@ hw_status hw_append_step(hw_ctx *ctx, int32_t layer, const void *k, const void *
   }
   ctx->plan.pending[layer] = 1;
   return HW_OK;
+}
+
+hw_status hw_decode_step(hw_ctx *ctx, int32_t layer, const void *k, const void *v, const float *q,
+                         float *out, float *lse, void *stream) {
+  if (!ctx) return HW_ERR_INVALID_ARG;
+  const hw_config &g = ctx->cfg;
+  const Plan &p = ctx->plan;
+  if (!p.active) return ctx->fail(HW_ERR_INVALID_ARG, "no step plan is active");
+  if (layer < 0 || layer >= g.n_layers) return ctx->fail(HW_ERR_INVALID_ARG, "layer out of range");
+  if (p.pending[layer])
+    return ctx->fail(HW_ERR_INVALID_ARG, "this layer's planned step is appended but not decoded yet");
+  if (!p.fusable)
+    return ctx->fail(HW_ERR_INVALID_ARG, "the plan has a growing block in no view, or more rows than one "
+                                         "decode workgroup holds: use hw_append_step and hw_concurrent_decode");
+  if (!k || !v) return ctx->fail(HW_ERR_INVALID_ARG, "k/v NULL");
+  if (((uintptr_t)k | (uintptr_t)v) % 16) return ctx->fail(HW_ERR_INVALID_ARG, "k/v must be 16-byte aligned");
+  if (!q || !out) return ctx->fail(HW_ERR_INVALID_ARG, "q/out NULL");
+  if (!ctx->ws) return ctx->fail(HW_ERR_WORKSPACE, "no workspace set");
+  return decode_planned(ctx, layer, 1, q, out, lse, (hipStream_t)stream, workspace_partials(ctx), k, v);
 }
 
 hw_status hw_plan_end(hw_ctx *ctx, void *stream) {

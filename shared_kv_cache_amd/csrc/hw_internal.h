@@ -95,6 +95,16 @@ struct DecodeArgs {
   const int32_t *plan_step;
   int32_t plan_pending;
   int32_t plan_n_steps;
+  // Fused step (hw_decode_step; null fuse_k: none): the layer's planned append, written by
+  // the decode's own waves before they read the groups it fills. fuse_blocks[i] = {base
+  // length, tokens per step, first input row, index in the group list of the block's first
+  // group}; fuse_overflow is set to 1 by a step past the window (nothing is then written).
+  const void *fuse_k;      // [rows][n_kv_heads][head_dim] bf16, rows in planned-block order
+  const void *fuse_v;
+  const float2 *fuse_trig; // [max_position][head_dim/2] (cos, sin)
+  const int32_t *fuse_blocks;
+  int32_t *fuse_overflow;
+  int32_t fuse_n_blocks;
   // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];

@@ -148,6 +148,59 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
   }
 }
 
+// One key chunk of one token and head: its 8 rotated pairs (dims 8*c8 + e and D/2 + 8*c8 + e,
+// e < 8) from the raw key row ksrc (head_dim elements) and the position's (cos, sin) row
+// trig (D/2 pairs), stored into slot u of the head's group kg, the chunk's 8 dims of one
+// token being contiguous in the K layout (16 or 32 bytes).
+template <typename KV, int D>
+__device__ __forceinline__ void put_key_chunk(const KV *ksrc, const float2 *trig, KV *kg, int u, int c8) {
+  constexpr int kVec = 16 / (int)sizeof(KV);   // elements per 16-byte access
+  static_assert(8 % kVec == 0, "8-element chunks in 16-byte accesses");
+  uint4 kl[8 / kVec], kh[8 / kVec];
+#pragma unroll
+  for (int j = 0; j < 8 / kVec; ++j) {
+    kl[j] = *reinterpret_cast<const uint4 *>(ksrc + 8 * c8 + kVec * j);
+    kh[j] = *reinterpret_cast<const uint4 *>(ksrc + D / 2 + 8 * c8 + kVec * j);
+  }
+  float4 cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cs[j] = reinterpret_cast<const float4 *>(trig + 8 * c8)[j];
+  const KV *x0 = reinterpret_cast<const KV *>(kl), *x1 = reinterpret_cast<const KV *>(kh);
+  const float *cf = reinterpret_cast<const float *>(cs);
+  float lo[8], hi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a0, a1;
+    if constexpr (sizeof(KV) == 2) {
+      a0 = __uint_as_float((uint32_t)(*(const uint16_t *)&x0[e]) << 16);
+      a1 = __uint_as_float((uint32_t)(*(const uint16_t *)&x1[e]) << 16);
+    } else {
+      a0 = x0[e];
+      a1 = x1[e];
+    }
+    rotate_pair(a0, a1, cf[2 * e], cf[2 * e + 1], lo[e], hi[e]);
+  }
+  KV *klo = kg + k_index(u, 8 * c8), *khi = kg + k_index(u, D / 2 + 8 * c8);
+  if constexpr (sizeof(KV) == 2) {
+    uint4 wlo, whi;
+    wlo.x = bf16_rne_bits(lo[0]) | ((uint32_t)bf16_rne_bits(lo[1]) << 16);
+    wlo.y = bf16_rne_bits(lo[2]) | ((uint32_t)bf16_rne_bits(lo[3]) << 16);
+    wlo.z = bf16_rne_bits(lo[4]) | ((uint32_t)bf16_rne_bits(lo[5]) << 16);
+    wlo.w = bf16_rne_bits(lo[6]) | ((uint32_t)bf16_rne_bits(lo[7]) << 16);
+    whi.x = bf16_rne_bits(hi[0]) | ((uint32_t)bf16_rne_bits(hi[1]) << 16);
+    whi.y = bf16_rne_bits(hi[2]) | ((uint32_t)bf16_rne_bits(hi[3]) << 16);
+    whi.z = bf16_rne_bits(hi[4]) | ((uint32_t)bf16_rne_bits(hi[5]) << 16);
+    whi.w = bf16_rne_bits(hi[6]) | ((uint32_t)bf16_rne_bits(hi[7]) << 16);
+    *reinterpret_cast<uint4 *>(klo) = wlo;
+    *reinterpret_cast<uint4 *>(khi) = whi;
+  } else {
+    reinterpret_cast<float4 *>(klo)[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    reinterpret_cast<float4 *>(klo)[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+    reinterpret_cast<float4 *>(khi)[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    reinterpret_cast<float4 *>(khi)[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // plan_append: the append of one planned step of one layer; one workgroup per input row.
 // Every thread reads the layer's step counter s and nothing here writes it (the kernel
@@ -158,8 +211,6 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AppendArgs a) {
 template <typename KV, int D>
 __global__ __launch_bounds__(256) void plan_append_kernel(PlanAppendArgs a) {
   constexpr int kChunks = D / 16;
-  constexpr int kVec = 16 / (int)sizeof(KV);   // elements per 16-byte access
-  static_assert(8 % kVec == 0, "8-element chunks in 16-byte accesses");
   const int hkv = a.n_kv_heads;
   const KV *__restrict__ ksrc = static_cast<const KV *>(a.k_src);
   const KV *__restrict__ vsrc = static_cast<const KV *>(a.v_src);
@@ -202,53 +253,8 @@ __global__ __launch_bounds__(256) void plan_append_kernel(PlanAppendArgs a) {
   // Keys: thread -> (head, 8-dim chunk).
   for (int it = threadIdx.x; it < hkv * kChunks; it += blockDim.x) {
     const int c8 = it % kChunks, h = it / kChunks;
-    const size_t src = src0 + (size_t)h * D;
-    uint4 kl[8 / kVec], kh[8 / kVec];
-#pragma unroll
-    for (int j = 0; j < 8 / kVec; ++j) {
-      kl[j] = *reinterpret_cast<const uint4 *>(ksrc + src + 8 * c8 + kVec * j);
-      kh[j] = *reinterpret_cast<const uint4 *>(ksrc + src + D / 2 + 8 * c8 + kVec * j);
-    }
-    float4 cs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      cs[j] = reinterpret_cast<const float4 *>(a.trig + (size_t)pos * (D / 2) + 8 * c8)[j];
-    const KV *x0 = reinterpret_cast<const KV *>(kl), *x1 = reinterpret_cast<const KV *>(kh);
-    const float *cf = reinterpret_cast<const float *>(cs);
-    float lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a0, a1;
-      if constexpr (sizeof(KV) == 2) {
-        a0 = __uint_as_float((uint32_t)(*(const uint16_t *)&x0[e]) << 16);
-        a1 = __uint_as_float((uint32_t)(*(const uint16_t *)&x1[e]) << 16);
-      } else {
-        a0 = x0[e];
-        a1 = x1[e];
-      }
-      rotate_pair(a0, a1, cf[2 * e], cf[2 * e + 1], lo[e], hi[e]);
-    }
-    // The chunk's 8 dims of one token are contiguous in the K layout (16 or 32 bytes).
-    KV *kg = kdst + (head0 + (size_t)h * a.page_groups) * (size_t)(32 * D);
-    KV *klo = kg + k_index(u, 8 * c8), *khi = kg + k_index(u, D / 2 + 8 * c8);
-    if constexpr (sizeof(KV) == 2) {
-      uint4 wlo, whi;
-      wlo.x = bf16_rne_bits(lo[0]) | ((uint32_t)bf16_rne_bits(lo[1]) << 16);
-      wlo.y = bf16_rne_bits(lo[2]) | ((uint32_t)bf16_rne_bits(lo[3]) << 16);
-      wlo.z = bf16_rne_bits(lo[4]) | ((uint32_t)bf16_rne_bits(lo[5]) << 16);
-      wlo.w = bf16_rne_bits(lo[6]) | ((uint32_t)bf16_rne_bits(lo[7]) << 16);
-      whi.x = bf16_rne_bits(hi[0]) | ((uint32_t)bf16_rne_bits(hi[1]) << 16);
-      whi.y = bf16_rne_bits(hi[2]) | ((uint32_t)bf16_rne_bits(hi[3]) << 16);
-      whi.z = bf16_rne_bits(hi[4]) | ((uint32_t)bf16_rne_bits(hi[5]) << 16);
-      whi.w = bf16_rne_bits(hi[6]) | ((uint32_t)bf16_rne_bits(hi[7]) << 16);
-      *reinterpret_cast<uint4 *>(klo) = wlo;
-      *reinterpret_cast<uint4 *>(khi) = whi;
-    } else {
-      reinterpret_cast<float4 *>(klo)[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
-      reinterpret_cast<float4 *>(klo)[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
-      reinterpret_cast<float4 *>(khi)[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
-      reinterpret_cast<float4 *>(khi)[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
-    }
+    put_key_chunk<KV, D>(ksrc + src0 + (size_t)h * D, a.trig + (size_t)pos * (D / 2),
+                         kdst + (head0 + (size_t)h * a.page_groups) * (size_t)(32 * D), u, c8);
   }
 }
 
@@ -802,9 +808,10 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // the offset table, both always allocated; the data goes unused. Loads issued
   // unconditionally keep the waits for each stage exact.
   // Step plan: planned appends of this layer so far (wave-uniform, scalar cache).
-  int pstep = 0;
+  int pstep = 0, pcount = 0;
   if constexpr (PLAN) {
-    const int c = *(const ConstInt *)a.plan_step + a.plan_pending;
+    pcount = *(const ConstInt *)a.plan_step;
+    const int c = pcount + a.plan_pending;
     pstep = c < a.plan_n_steps ? c : a.plan_n_steps;
   }
   int s_lo = 0, s_hi = -1;
@@ -856,6 +863,49 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   };
   S st, st2;   // st: the group being computed; st2 (NST = 2): the group in flight
   int dl_cur[RT], dl_next[RT];   // NST = 1: offsets of the lane's rows for groups i, i+1
+
+  // Fused step: this step's planned append. Every (KV head, group) is read by exactly one
+  // wave, so the wave whose run holds a group that the step's tokens fall in writes those
+  // tokens for its KV head (the values, and the keys rotated at their positions, byte for
+  // byte as plan_append writes them), then makes its writes visible to its own later reads
+  // of the group. Positions of block i at count s: base + s * tps + j, j < tps; the block's
+  // groups are consecutive in the list from index g0, position p in group g0 + p / 32.
+  if constexpr (PLAN && std::is_same<KV, __bf16>::value) {
+    if (a.fuse_k != nullptr) {
+      if (pcount >= a.plan_n_steps) {   // past the window: nothing is written, the host reports it
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) a.fuse_overflow[0] = 1;
+      } else if (wcount > 0) {
+        bool wrote = false;
+        KV *const kw = const_cast<KV *>(kl), *const vw = const_cast<KV *>(vl);
+        for (int bi = 0; bi < a.fuse_n_blocks; ++bi) {
+          const ConstInt *fb = (const ConstInt *)a.fuse_blocks + 4 * bi;
+          const int base = fb[0], tps = fb[1], frow = fb[2], g0 = fb[3];
+          if (tps <= 0 || g0 < 0) continue;
+          const int pa = base + pcount * tps, pb = pa + tps - 1;
+          const int ga = max(g0 + (pa >> 5), wfirst), gz = min(g0 + (pb >> 5), wlast);
+          for (int gl = ga; gl <= gz; ++gl) {
+            const GDesc gd = load_desc<false, true>(hd.groups, gl, hd.desc_stride, pstep);
+            const size_t gbase = ((size_t)gd.x + head_groups) * (size_t)(32 * D);
+            const int p0 = max(pa, (gl - g0) * 32), p1 = min(pb, (gl - g0) * 32 + 31);
+            for (int pos = p0; pos <= p1; ++pos) {
+              const size_t src = ((size_t)(frow + pos - pa) * a.n_kv_heads + kvh) * D;
+              const KV *ks = static_cast<const KV *>(a.fuse_k) + src;
+              const KV *vs = static_cast<const KV *>(a.fuse_v) + src;
+              const int u = pos & 31;
+              for (int i = lane; i < D; i += 64) vw[gbase + v_index(u, i)] = vs[i];
+              if (lane < D / 16)
+                put_key_chunk<KV, D>(ks, a.fuse_trig + (size_t)pos * (D / 2), kw + gbase, u, lane);
+              wrote = true;
+            }
+          }
+        }
+        if (wrote) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
+      }
+    }
+  }
   if constexpr (COOP) {
     load_offsets(s_lo);
     fetch_group(st2, desc, kl, vl, head_groups, lane);

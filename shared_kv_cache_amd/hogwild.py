@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "HW_OK", 1: "HW_ERR_INVALID_ARG", 2: "HW_ERR_OUT_OF_PAGES",
 # every symbol the headers declare
 EXPORTS = ["hw_create", "hw_destroy", "hw_last_error", "hw_workspace_bytes", "hw_set_workspace",
            "hw_append_kv", "hw_set_views", "hw_concurrent_decode", "hw_concurrent_decode_tokens",
-           "hw_concurrent_decode_noalloc", "hw_reset_block", "hw_plan_steps", "hw_append_step", "hw_plan_end",
+           "hw_concurrent_decode_noalloc", "hw_reset_block", "hw_plan_steps", "hw_append_step", "hw_decode_step",
+           "hw_plan_end",
            "hw_set_split", "hw_block_info", "hw_free_pages", "hw_debug_reserve",
            "hw_debug_resolve", "hw_debug_kernel_events", "hw_debug_kernel_elapsed",
            "hw_debug_stream_read", "hw_debug_partition"]
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hw_reset_block": (c_int, [c_void_p, c_int32]),
         "hw_plan_steps": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_void_p]),
         "hw_append_step": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+        "hw_decode_step": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p]),
         "hw_plan_end": (c_int, [c_void_p, c_void_p]),
         "hw_set_split": (c_int, [c_void_p, c_int32]),
         "hw_block_info": (c_int, [c_void_p, c_int32, c_int32, P32, P32, c_int32, P32]),
@@ -201,6 +204,13 @@ def hw_plan_steps(ctx, n_steps: int, block_ids: Sequence[int], tokens_per_step: 
 def hw_append_step(ctx, layer: int, k_ptr: int, v_ptr: int, stream: int) -> None:
     _check(ctx, load_library().hw_append_step(ctx, layer, c_void_p(k_ptr), c_void_p(v_ptr),
                                               c_void_p(stream)))
+
+
+def hw_decode_step(ctx, layer: int, k_ptr: int, v_ptr: int, q_ptr: int, out_ptr: int,
+                   lse_ptr: Optional[int], stream: int) -> None:
+    _check(ctx, load_library().hw_decode_step(ctx, layer, c_void_p(k_ptr), c_void_p(v_ptr),
+                                              c_void_p(q_ptr), c_void_p(out_ptr),
+                                              c_void_p(lse_ptr or 0), c_void_p(stream)))
 
 
 def hw_plan_end(ctx, stream: int) -> None:
@@ -381,13 +391,25 @@ class HogwildCache:
 
     def append_step(self, layer: int, k, v) -> None:
         """One planned step's tokens of one layer: k, v [rows, n_kv_heads, head_dim]."""
+        self._kv_step(k, v)
+        hw_append_step(self.ctx, layer, k.data_ptr(), v.data_ptr(), self._stream())
+
+    def _kv_step(self, k, v) -> None:
         shape = (self.plan_rows, self.n_kv_heads, self.head_dim)
         for t in (k, v):
             if t.dtype != self.kv_torch_dtype or tuple(t.shape) != shape or not t.is_contiguous() \
                     or t.device != self.device:
                 raise HwError(HW_ERR_INVALID_ARG, f"k/v must be contiguous {self.kv_torch_dtype} "
                                                   f"{shape} on {self.device}")
-        hw_append_step(self.ctx, layer, k.data_ptr(), v.data_ptr(), self._stream())
+
+    def decode_step(self, layer: int, k, v, q, out=None, lse=None, want_lse: bool = True):
+        """A planned step of one layer, append fused into the decode: k, v as append_step,
+        q (and out, lse) as decode."""
+        self._kv_step(k, v)
+        out, lse = self._io(q, out, lse, want_lse, (self.n_workers, self.n_q_heads, self.head_dim))
+        hw_decode_step(self.ctx, layer, k.data_ptr(), v.data_ptr(), q.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if lse is not None else None, self._stream())
+        return out, lse
 
     def plan_end(self) -> None:
         hw_plan_end(self.ctx, self._stream())

@@ -240,3 +240,107 @@ def test_plan_step_order_rules():
     for b in wl.inprogress:
         assert cache.block_info(b, 0)[0] == wl.lengths[b] + 3
     cache.close()
+
+
+def _pool_bits(cache):
+    torch.cuda.synchronize()
+    return (cache.k_pool.view(torch.int16).cpu(), cache.v_pool.view(torch.int16).cpu())
+
+
+def test_fused_step_equals_append_then_decode():
+    # hw_decode_step against hw_append_step + hw_concurrent_decode on two caches in the same
+    # state: six steps on two layers of the small workload (blocks crossing a page and a
+    # group boundary, starting empty, taking two tokens a step; 20 rows: the 8-wave kernel).
+    # Outputs, lse and every pool byte must agree bit for bit, and the lengths after the plan.
+    wl = _small_workload(2)
+    caches = [make_cache(wl, max_splits=64) for _ in range(2)]
+    tps = [1, 1, 1, 2]
+    for c in caches:
+        for layer in range(2):
+            fill_layer(c, wl, layer)
+        c.set_views(wl.views())
+        c.plan_steps(6, wl.inprogress, tps)
+    rng = np.random.default_rng(11)
+    for step in range(1, 7):
+        for layer in range(2):
+            k, v = (kv_tensor(W.round_to_bf16_values(rng.standard_normal((sum(tps), 8, 128),
+                                                                       dtype=np.float32)), "bf16")
+                    for _ in range(2))
+            q = torch.from_numpy(wl.q(layer, step)).to(DEV)
+            caches[0].append_step(layer, k, v)
+            o0, l0 = caches[0].decode(layer, q)
+            o1, l1 = caches[1].decode_step(layer, k, v, q)
+            torch.cuda.synchronize()
+            assert torch.equal(o0, o1) and torch.equal(l0, l1), (step, layer)
+    a, b = _pool_bits(caches[0]), _pool_bits(caches[1])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for c in caches:
+        c.plan_end()
+    for blk, t in zip(wl.inprogress, tps):
+        for layer in range(2):
+            assert caches[1].block_info(blk, layer)[0] == wl.lengths[blk] + 6 * t
+    _say("fused small: 12 steps bitwise equal to append + decode, pools equal")
+    for c in caches:
+        c.close()
+
+
+def test_w8_32k_fused_step_graph_equals_two_call_steps():
+    # The w8_32k step with its appends fused into the decodes (40 rows: the cooperative
+    # kernel), captured once as a HIP graph and replayed three times, against the same steps
+    # run eagerly with hw_append_step + hw_concurrent_decode: bitwise equal outputs and pools.
+    plan = 4
+    wl, ca = _w8_cache(plan)
+    _, cb = _w8_cache(plan)
+    L, n = wl.n_layers, wl.n_workers
+    kv = [[tuple(kv_tensor(x, "bf16") for x in wl.step_kv(layer, s)) for layer in range(L)]
+          for s in range(1, 4)]
+    qs = [[torch.from_numpy(wl.q(layer, s)).to(DEV) for layer in range(L)] for s in range(1, 4)]
+    outs = [torch.empty((n, wl.n_q_heads, wl.head_dim), device=DEV) for _ in range(L)]
+    lses = [torch.empty((n, wl.n_q_heads), device=DEV) for _ in range(L)]
+    eager = []
+    for s in range(3):
+        for layer in range(L):
+            ca.append_step(layer, *kv[s][layer])
+            ca.decode(layer, qs[s][layer], out=outs[layer], lse=lses[layer])
+        torch.cuda.synchronize()
+        eager.append(([o.clone() for o in outs], [x.clone() for x in lses]))
+    kbuf = [torch.empty_like(kv[0][layer][0]) for layer in range(L)]
+    vbuf = [torch.empty_like(kv[0][layer][1]) for layer in range(L)]
+    qbuf = [torch.empty_like(qs[0][layer]) for layer in range(L)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        for layer in range(L):
+            cb.decode_step(layer, kbuf[layer], vbuf[layer], qbuf[layer], out=outs[layer],
+                           lse=lses[layer])
+    torch.cuda.synchronize()
+    for s in range(3):
+        for layer in range(L):
+            kbuf[layer].copy_(kv[s][layer][0])
+            vbuf[layer].copy_(kv[s][layer][1])
+            qbuf[layer].copy_(qs[s][layer])
+            outs[layer].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer in range(L):
+            assert torch.equal(outs[layer], eager[s][0][layer]), (s, layer)
+            assert torch.equal(lses[layer], eager[s][1][layer]), (s, layer)
+        _say(f"fused replay {s + 1}: equal to the two-call eager step")
+    a, b = _pool_bits(ca), _pool_bits(cb)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # past the window: the fifth fused step writes nothing and is reported
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    with pytest.raises(H.HwError) as e:
+        cb.plan_end()
+    assert e.value.status == H.HW_ERR_INVALID_ARG and "dropped" in e.value.message
+    ca.plan_end()
+    for blk in wl.inprogress:
+        for layer in range(L):
+            assert cb.block_info(blk, layer)[0] == wl.lengths[blk] + plan
+    ca.close()
+    cb.close()

@@ -83,9 +83,9 @@ def test_workspace_size_formula(ctx):
     expect += al(al(16 * 4 * 4) + al(max_groups * 8 * 4))   # up to 8 ints per group descriptor
     expect += al(256 * 2 * rows * d * 4)
     expect += al(256 * 2 * rows * 4)
-    # step-plan region: counters (2 layers + overflow flag), {d0, rate} offsets, 4-int
-    # descriptors
-    expect += al(al(3 * 4) + al(16 * 4 * 2 * 4) + al(max_groups * 4 * 4))
+    # step-plan region: counters (2 layers + overflow flag), the fused step's table (64
+    # blocks x 4 ints), {d0, rate} offsets, 4-int descriptors
+    expect += al(al(3 * 4) + al(64 * 4 * 4) + al(16 * 4 * 2 * 4) + al(max_groups * 4 * 4))
     assert H.hw_workspace_bytes(ctx) == expect
     # several query tokens per worker: partials for every (worker, token, head) row
     c3 = H.hw_create(make_cfg(max_query_tokens=3))
@@ -503,6 +503,9 @@ def test_step_plan_validation_before_any_change(ctx):
     with pytest.raises(H.HwError) as e:
         H.hw_append_step(ctx, 0, FAKE_K, FAKE_V, 0)
     assert e.value.status == H.HW_ERR_INVALID_ARG
+    with pytest.raises(H.HwError) as e:
+        H.hw_decode_step(ctx, 0, FAKE_K, FAKE_V, FAKE_K, FAKE_V, None, 0)
+    assert e.value.status == H.HW_ERR_INVALID_ARG and "no step plan" in e.value.message
     with pytest.raises(H.HwError) as e:
         H.hw_plan_end(ctx, 0)
     assert e.value.status == H.HW_ERR_INVALID_ARG
