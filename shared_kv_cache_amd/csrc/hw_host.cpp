@@ -369,10 +369,12 @@ void partition_bounds(const uint8_t *first, int32_t G, int32_t n, double alpha, 
 }
 
 // Weight of a block entry in group units, by kernel shape. Cooperative kernels (33..64 bf16
-// rows) rotate every block of a partition before streaming it; measured on MI355X, a
-// partition's extra block costs it about the time of this many groups.
+// rows) rotate every block of a partition before streaming it, and under a fused step plan
+// the waves whose groups take the step's tokens also write them first. Measured on MI355X
+// (w8_32k, 8 growing blocks): weights 2, 3, 4, 6, 8 give 0.345, 0.340, 0.331, 0.332 and
+// 0.338 ms per fused step (0.364 and 0.353 ms for 2 and 4 with the append as its own launch).
 #ifndef HW_SPLIT_ALPHA_COOP
-#define HW_SPLIT_ALPHA_COOP 2.0
+#define HW_SPLIT_ALPHA_COOP 4.0
 #endif
 #ifndef HW_SPLIT_ALPHA_8W
 #define HW_SPLIT_ALPHA_8W 0.0
