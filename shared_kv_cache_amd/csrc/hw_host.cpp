@@ -394,8 +394,10 @@ int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows, int32_t n_n
   // Several query tokens per worker do more work per byte; filling every CU pays there:
   // w4_16k with 4 tokens runs 11% faster with 10 partitions (240 workgroups) than with 8,
   // w8_32k 19% faster with 4 (256) than with 3; one more partition each spills past one
-  // workgroup per CU and is slower.
-  const int32_t target = n_new > 1 ? c->num_cus : 3 * c->num_cus / 4;
+  // workgroup per CU and is slower. The cooperative (4-wave) kernels also fill every CU:
+  // w8_32k's fused step takes 0.3295 ms with 32 partitions, 0.3312 with 24, 0.3338 with 28.
+  const bool coop = hw::decode_waves(c->cfg.kv_dtype, rows, n_new) == 4;
+  const int32_t target = (n_new > 1 || coop) ? c->num_cus : 3 * c->num_cus / 4;
   int32_t s = std::max(1, target / per_head);
   // At least 4 groups a partition. Small caches still want the parallelism: on w2_4k (142
   // groups a head) 24 partitions beat 17 (at least 8 groups each) by 2% per step, and 12 by 6%.
