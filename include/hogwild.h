@@ -183,7 +183,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
 
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): hw_concurrent_decode with the split partials kept in a
- * static device array of the library (8 MiB per GPU, held until the process ends) instead
+ * static device array of the library (16 MiB per GPU, held until the process ends) instead
  * of the workspace. Same arguments, kernels and results as hw_concurrent_decode; it calls no
  * hipMalloc, hipFree or other routine that allocates device or pinned memory (the pinned
  * staging ring and the array's address are set up by hw_set_workspace). Every call on one
@@ -191,7 +191,7 @@ hw_status hw_concurrent_decode(hw_ctx *ctx, int32_t layer, const float *q, float
  * start at zero): calls that overlap on one GPU, from any context or stream, race.
  * Errors: as hw_concurrent_decode; HW_ERR_WORKSPACE when the partials of the partition count
  * the decode would use (partitions x n_kv_heads x n_workers x (n_q_heads / n_kv_heads) x
- * (head_dim + 1) fp32) do not fit 8 MiB: force fewer with hw_set_split. */
+ * (head_dim + 1) fp32) do not fit 16 MiB: force fewer with hw_set_split. */
 hw_status hw_concurrent_decode_noalloc(hw_ctx *ctx, int32_t layer, const float *q, float *out,
                                        float *lse, void *stream);
 

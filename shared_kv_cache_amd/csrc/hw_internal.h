@@ -173,7 +173,7 @@ hipError_t launch_merge(int head_dim, const MergeArgs &a, hipStream_t s);
 
 // Size of the static scratch that hw_concurrent_decode_noalloc keeps its split partials in,
 // and its device address on the current device.
-constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchBytes = (size_t)16 << 20;
 hipError_t scratch_address(void **ptr);
 hipError_t launch_stream_read(const void *src, size_t bytes, float *sink, int n_blocks, hipStream_t s,
                               hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -37,7 +37,7 @@ def _both(cache, q):
 
 
 def test_noalloc_decode_equals_the_workspace_decode():
-    # The w8_32k layer (8 workers x 8 heads = 64 rows per KV head, 24 partitions: 6.3 MB
+    # The w8_32k layer (8 workers x 8 heads = 64 rows per KV head, 32 partitions: 8.5 MB
     # of partials), then a smaller input on the same array: three workers' views.
     wl = W.make("w8_32k", n_layers=1)
     cache = make_cache(wl)
@@ -75,7 +75,7 @@ def test_noalloc_decode_equals_the_workspace_decode():
         np.testing.assert_array_equal(lse.cpu().numpy(), l_ws)
     # partials beyond the array: refused before anything is enqueued
     cache.set_views(views)
-    H.hw_set_split(cache.ctx, 200)          # 200 x 8 x 64 x 129 x 4 B = 52.8 MB > 8 MiB
+    H.hw_set_split(cache.ctx, 200)          # 200 x 8 x 64 x 129 x 4 B = 52.8 MB > 16 MiB
     out8 = torch.zeros((8, wl.n_q_heads, wl.head_dim), device=DEV)
     q8 = torch.from_numpy(q_all).to(DEV)
     with pytest.raises(H.HwError) as e:
