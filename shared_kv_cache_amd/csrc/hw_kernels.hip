@@ -566,6 +566,11 @@ __device__ __forceinline__ int wave_slot() { return __builtin_amdgcn_readfirstla
 // for its vector loads, so the K/V loads and stage fills in flight keep streaming across it.
 // (__syncthreads waits for every outstanding vector load first.) The memory clobber keeps
 // the compiler from moving memory accesses across it.
+// s_waitcnt operand that waits for every vector memory and LDS/scalar access of the wave
+// (gfx9 encoding: vmcnt 0 in bits 3:0 and 15:14, expcnt 7 in bits 6:4, lgkmcnt 0 in bits
+// 11:8). Issued through the builtin, the compiler's own wait tracking sees it.
+constexpr unsigned kWaitAll = 0x0070;
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -945,17 +950,30 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   // Rotation of one row's query by delta = q_pos(w) - offset(w, block), for the 8 pairs
   // (j, j + D/2), j = j0 .. j0 + 7: the angle delta * theta_j is reduced to a fraction of a
   // turn in fp64; the sine and cosine of that fraction come from the hardware's fp32 units.
-  auto rotate8 = [&](const float *qrow, int j0, int dl, float *lo, float *hi) __attribute__((always_inline)) {
+  // rotate8r takes the pairs' values (x0: dims j, x1: dims j + D/2) and frequencies from
+  // registers; rotate8 reads them from the staged row and the frequency table.
+  auto rotate8r = [&](const float *x0, const float *x1, const double *fv, int dl, float *lo,
+                      float *hi) __attribute__((always_inline)) {
     const double ddl = (double)dl;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double turns = ddl * sm_freq[j0 + e];
+      const double turns = ddl * fv[e];
       const float fr = (float)(turns - __builtin_rint(turns));
       const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
-      const float x0 = qrow[j0 + e], x1 = qrow[D / 2 + j0 + e];
-      lo[e] = x0 * cs - x1 * sn;
-      hi[e] = x1 * cs + x0 * sn;
+      lo[e] = x0[e] * cs - x1[e] * sn;
+      hi[e] = x1[e] * cs + x0[e] * sn;
     }
+  };
+  auto rotate8 = [&](const float *qrow, int j0, int dl, float *lo, float *hi) __attribute__((always_inline)) {
+    float x0[8], x1[8];
+    double fv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x0[e] = qrow[j0 + e];
+      x1[e] = qrow[D / 2 + j0 + e];
+      fv[e] = sm_freq[j0 + e];
+    }
+    rotate8r(x0, x1, fv, dl, lo, hi);
   };
   // COOP: rotate every (segment, row) of a phase of nseg segments, all threads together. One
   // item is (segment, row tile, chunk pair, lane).
@@ -998,6 +1016,18 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   }
   int cur_seg = -1;
 
+  // The visibility part of entering a group (NST = 1): the lane's rows' offsets into the
+  // group's block.
+  auto enter_rows = [&](const int (&delta)[RT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int dl = row_offset(delta[rt], row_back[rt]);
+      rowoff[rt] = dl;
+      rowvis[rt] = row_ok[rt] && dl >= 0;
+      rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
+    }
+  };
+
   // One group: visibility and (NST = 1, new segment) rotation, scores, online softmax, PV.
   // seg_lo: first segment of the current phase (COOP); delta: the lane's rows' offsets for
   // the group's block (NST = 1).
@@ -1020,13 +1050,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
         }
       }
     } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int dl = row_offset(delta[rt], row_back[rt]);
-        rowoff[rt] = dl;
-        rowvis[rt] = row_ok[rt] && dl >= 0;
-        rowmask[rt] = __builtin_amdgcn_ballot_w64(row_ok[rt] && dl < 0) != 0;
-      }
+      enter_rows(delta);
       if (seg != cur_seg) {
         cur_seg = seg;
 #pragma unroll
@@ -1157,16 +1181,57 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // A wave raises its priority while it takes its group from the stage and issues the next
     // fill, and drops it to compute: the other wave on the SIMD, mid-compute, then yields
     // the issue slots to the one whose data has landed, which keeps the fills going.
-    if (wcount > 0) enter(st, 0, dl_cur);   // the first rotation, before any fill
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    if (wcount > 1) {
-      const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
-      F::template load_lds<!MT>(kl + gb, vl + gb, lane, stage);
+    //
+    // Group 0: the first rotation's inputs are read from LDS into registers, then group 1's
+    // fill goes out, then the rotation runs on the registers while both groups stream. The
+    // compiler cannot tell which of a mix of pending fills and ordinary loads has completed,
+    // so group 0's scores wait for group 1's fill as well. With several tokens per worker
+    // the wave first waits for group 0 alone (its row blocks share the groups through L2,
+    // and group 0 has mostly landed by then), so that group 0 is computed while group 1
+    // streams; a one-token decode's group 0 comes from HBM in the first burst of requests,
+    // and waiting for it would hold group 1's request back. (Measured on MI355X, against
+    // the first rotation before the fill: w4_16k 1.400 against 1.450 ms per step; w4_16k
+    // with 4 tokens 1.770 against 1.831 ms.)
+    {
+      float qa[RT][NC / 2][8], qb[RT][NC / 2][8];
+      double fa[NC / 2][8];
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fa[c][e] = sm_freq[32 * c + 8 * grp + e];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qa[rt][c][e] = qrows[(rt * 16 + col) * QSTRIDE + 32 * c + 8 * grp + e];
+            qb[rt][c][e] = qrows[(rt * 16 + col) * QSTRIDE + D / 2 + 32 * c + 8 * grp + e];
+          }
+      if constexpr (MT) __builtin_amdgcn_s_waitcnt(kWaitAll);   // group 0 (and the reads above)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      if (wcount > 1) {
+        const size_t gb = ((size_t)next.x + head_groups) * (size_t)(32 * D);
+        F::template load_lds<!MT>(kl + gb, vl + gb, lane, stage);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (wcount > 0) {
+        enter_rows(dl_cur);
+        cur_seg = st.desc_y >> 8;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int c = 0; c < NC / 2; ++c) {
+            float lo[8], hi[8];
+            rotate8r(qa[rt][c], qb[rt][c], fa[c], rowoff[rt] < 0 ? 0 : rowoff[rt], lo, hi);
+            qreg[rt][c] = rowvis[rt] ? F::make_q(lo) : F::zero_q();
+            qreg[rt][c + NC / 2] = rowvis[rt] ? F::make_q(hi) : F::zero_q();
+          }
+        compute(st, 0);
+      }
     }
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (wcount > 0) compute(st, 0);
     for (int i = 1; i < wcount; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
