@@ -716,6 +716,8 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   __shared__ double sm_freq[D / 2];
   __shared__ float sm_m[NW][16 * RT];
   __shared__ float sm_l[NW][16 * RT];
+  __shared__ __attribute__((aligned(16))) float sm_f[16 * RT][NW];   // combine factors per row
+  __shared__ float sm_inv[16 * RT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1343,36 +1345,55 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     for (int dt = 0; dt < NDT; ++dt) buf[wave * WSTRIDE + (rt * NDT + dt) * 64 + lane] = o[rt][dt];
   lds_barrier();
 
+  // Per row, once: the common maximum, each wave's factor 2^(m_t - max), 1 / sum and the
+  // normaliser (lse); then every output slot is the factor-weighted sum of the waves' parts.
   const bool direct = a.n_splits == 1;
-  for (int q = tid; q < SLOTS; q += NT) {
-    const int rt = q / (NDT * 64), dt = (q / 64) % NDT, ln = q % 64;
-    const int r = rt * 16 + (ln & 15);
-    if (r >= nrows) continue;
+  if (tid < 16 * RT) {
+    const int r = tid;
     float mm = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NW; ++t) mm = fmaxf(mm, sm_m[t][r]);
-    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
     float L = 0.0f;
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
       const float mt = sm_m[t][r];
       const float f = mt == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt - mm);
-      x += buf[t * WSTRIDE + q] * f;
+      sm_f[r][t] = f;
       L += sm_l[t][r] * f;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    sm_inv[r] = L > 0.0f ? 1.0f / L : 0.0f;
+    if (r < nrows) {
+      const int rr = row0 + r;
+      if (direct) {
+        const int wt = tok_of(rr), h = kvh * a.group + rr - wt * a.group;
+        if (a.lse)
+          a.lse[(size_t)wt * a.n_q_heads + h] =
+              L > 0.0f ? (mm + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+      } else {
+        const size_t prow = ((size_t)split * a.n_kv_heads + kvh) * a.rows + rr;
+        a.part_lse[prow] = L > 0.0f ? mm + __log2f(L) : -INFINITY;
+      }
+    }
+  }
+  lds_barrier();
+  constexpr int ITER = (SLOTS + NT - 1) / NT;
+#pragma unroll
+  for (int k = 0; k < ITER; ++k) {
+    const int q = tid + k * NT;
+    const int rt = q / (NDT * 64), dt = (q / 64) % NDT, ln = q % 64;
+    const int r = rt * 16 + (ln & 15);
+    if (q >= SLOTS || r >= nrows) continue;
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NW; ++t) x += buf[t * WSTRIDE + q] * sm_f[r][t];
+    const float inv = sm_inv[r];
     const int rr = row0 + r;
     float *dst;
     if (direct) {
       const int wt = tok_of(rr), h = kvh * a.group + rr - wt * a.group;
       dst = a.out + ((size_t)wt * a.n_q_heads + h) * D;
-      if (dt == 0 && (ln >> 4) == 0 && a.lse)
-        a.lse[(size_t)wt * a.n_q_heads + h] =
-            L > 0.0f ? (mm + __log2f(L)) * 0.69314718055994531f : -INFINITY;
     } else {
-      const size_t prow = ((size_t)split * a.n_kv_heads + kvh) * a.rows + rr;
-      dst = a.part_o + prow * D;
-      if (dt == 0 && (ln >> 4) == 0) a.part_lse[prow] = L > 0.0f ? mm + __log2f(L) : -INFINITY;
+      dst = a.part_o + (((size_t)split * a.n_kv_heads + kvh) * a.rows + rr) * D;
     }
     *reinterpret_cast<float4 *>(dst + 16 * dt + 4 * (ln >> 4)) =
         make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
