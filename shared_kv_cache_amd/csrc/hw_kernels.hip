@@ -681,12 +681,13 @@ __device__ __forceinline__ Head load_head(int sp) {
 // offsets are affine in the number of planned appends of the layer, read from the device
 // at launch (see load_desc and delta_at), so the launch needs no host-side tables update
 // from step to step.
-template <typename KV, int D, int RT, int NW, int NST, bool WIDE, bool MT, bool PLAN>
+template <typename KV, int D, int RT, int NW, int NST, bool WIDE, bool MT, bool PLAN, bool LATE = false>
 __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArgs a) {
   static_assert(NST == 1 || NST == 2, "one or two stages");
   static_assert(!WIDE || NST == 1, "wide descriptors: single-stage kernels");
   static_assert(!(WIDE && MT), "wide descriptors: one token per worker");
   static_assert(!(PLAN && (WIDE || MT)), "step plans: narrow descriptors, one token");
+  static_assert(!LATE || (WIDE && NST == 1 && std::is_same<KV, __bf16>::value), "late group 0: staged wide kernels");
   constexpr bool COOP = NST == 2;
   using F = Frag<KV, D>;
   using S = Stage<KV, D>;
@@ -926,7 +927,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     // LDSST: the queries land before group 0 is requested, ahead of the flood of every
     // wave's K/V loads (they gate the barrier below)
     if constexpr (LDSST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    fetch_group(st, desc, kl, vl, head_groups, lane);
+    if constexpr (!LATE) fetch_group(st, desc, kl, vl, head_groups, lane);
     wide_rows(dl_cur, ow);
   } else if constexpr (LDSST) {
     // narrow descriptors: the offsets of groups 0 and 1 are vector loads, in before group 0
@@ -954,6 +955,12 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
   if constexpr (COOP) store_offsets();
   if (tid < D / 2) sm_freq[tid] = fq;
   lds_barrier();   // the first groups' loads stay in flight
+  // LATE (waves of at most about one group): group 0 is requested only now, once every wave's
+  // queries are staged. With nothing to overlap it with, an early request only delays the
+  // other waves' queries behind the first burst of K/V loads (w2_4k: 0.352 against 0.364 ms
+  // per step); with several groups a wave, the early request wins (w4_16k: 1.373 against
+  // 1.462 ms).
+  if constexpr (LATE) fetch_group(st, desc, kl, vl, head_groups, lane);
 
   // Rotation of one row's query by delta = q_pos(w) - offset(w, block), for the 8 pairs
   // (j, j + D/2), j = j0 .. j0 + 7: the angle delta * theta_j is reduced to a fraction of a
@@ -1543,8 +1550,12 @@ static hipError_t launch_decode_bf16(int rt, const DecodeArgs &a, dim3 grid, hip
       return hipSuccess;
     }
   }
-  if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
+  // at most about 1.5 groups for each of a workgroup's 8 waves: group 0 requested late
+  const bool late = wide && a.n_groups <= 12 * a.n_splits;
+  if (rt == 1 && wide && late) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT, false, !MT>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 1 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 1) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 1, 8, 1, false, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
+  else if (rt == 2 && wide && late) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT, false, !MT>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 2 && wide) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, !MT, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
   else if (rt == 2) hipExtLaunchKernelGGL((concurrent_decode_kernel<__bf16, D, 2, 8, 1, false, MT, false>), grid, b8, 0, s, e0, e1, 0, a);
   else if constexpr (MT) return hipErrorInvalidValue;   // several tokens: blocks of <= 32 rows
