@@ -38,7 +38,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "concurrent-attn decode worker-steps/s and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "shared_kv_cache_amd", "csrc", "hw_kernels.hip")
+# The sources that decide what the decode launches run: the kernels, the launch-argument
+# layout, and the host code that picks partitions, row blocks and kernel shapes.
+KERNEL_SRCS = [os.path.join(ROOT, "shared_kv_cache_amd", "csrc", f)
+               for f in ("hw_kernels.hip", "hw_internal.h", "hw_host.cpp")]
 WORKLOADS = ["tiny_fp32", "w2_4k", "w4_16k", "w8_32k", "w4_128k_sinks"]
 
 
@@ -46,9 +49,36 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string literals kept), so
+    that a change to comments alone leaves the hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):

@@ -2,11 +2,15 @@
 //
 //   rope_append          RoPE-on-insert of new tokens at block-local positions
 //                        [Hogwild! Inference paper summary, s5 steps 1-2; s9]
+//   plan_append          the same for one planned step of a step plan (positions from the
+//                        layer's device counter), and advance, which moves that counter on
 //   concurrent_decode    split-K attention of every (worker, [query token,] query head) row of one KV head
 //                        over a balanced range of 32-token groups, rotating each worker's
 //                        query once per block it enters [summary s5 steps 3-5; s9 kernel]
 //   lse_merge            log-sum-exp merge of the split partials [summary s9 "partial
 //                        result reduction"; s5 step 5 "aggregate in the softmax weighting"]
+//   stream_read          a plain streaming read, the bandwidth ceiling the decode is measured
+//                        against (debug entry point)
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16; v_mfma_f32_16x16x4_f32 for fp32 pools):
 //   scores   S^T[token slot, row] = K[slot, :] . Qrot^T[:, row]    A = K tile, B = Qrot
@@ -18,8 +22,8 @@
 // softmax needs only two cross-lane exchanges per 32 tokens. The pool layouts (hogwild.h)
 // put each lane's 16-byte operand at lane * 16 of a 1 KiB run, so every load is coalesced
 // and lands in operand layout with no shuffle: straight into registers, or (the 8-wave bf16
-// kernels with wide descriptors) through a per-wave LDS stage that LDS-DMA loads fill while
-// the wave computes the previous group.
+// kernels) through a per-wave LDS stage that LDS-DMA loads fill while the wave computes the
+// previous group.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
