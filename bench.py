@@ -114,8 +114,9 @@ def run_gpu(name, args, graph, plan):
     plan = plan and grows and kq == 1
     fused = plan and not getattr(args, "unfused", False)
     steps, reps = args.steps, args.repeats
-    # planned window: warm-up, the timed repeats, the kernel-event pass, graph warm-up
-    total_steps = args.warmup + reps * steps + steps + 4
+    # planned window: warm-up, the timed repeats, the kernel-event pass and its warm-up step,
+    # graph warm-up
+    total_steps = args.warmup + reps * steps + steps + 5
     extra = {"n_layers": args.layers} if args.layers > 0 else {}
     wl = W.make(name, steps=total_steps if grows else 0, **extra)
     n, hq, hkv, d, L = wl.n_workers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers
@@ -230,8 +231,11 @@ def run_gpu(name, args, graph, plan):
         torch.cuda.synchronize()
         ms.append(ev0.elapsed_time(ev1))
     t_tok1 = tokens_now()
-    # Kernel pass: the same steps run eagerly, the decode kernels recording start/stop events.
+    # Kernel pass: the same steps run eagerly, the decode kernels recording start/stop events
+    # (after one eager step unrecorded: the first eager launches after the replays run slow).
     gsave, g = g, None
+    run_steps(1)
+    torch.cuda.synchronize()
     H.hw_debug_kernel_events(cache.ctx, steps * L)
     torch.cuda.synchronize()
     run_steps(steps)
