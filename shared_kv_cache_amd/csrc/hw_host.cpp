@@ -82,6 +82,7 @@ struct Plan {
   // hw_decode_step: every growing planned block is in some view (its groups are in the
   // list, so some decode wave writes each of its tokens) and the decode has one row block
   bool fusable = false;
+  int32_t fuse_gmin = 0, fuse_gmax = -1;    // group-list range the window's appends fall in
   // per layer: 1 while the step's append is enqueued and its decode not yet (the layer's
   // counter advances after that decode)
   std::vector<uint8_t> pending;
@@ -774,6 +775,7 @@ struct DecodeTables {
   const int32_t *fuse_blocks = nullptr;
   int32_t *fuse_overflow = nullptr;
   int32_t fuse_n_blocks = 0;
+  int32_t fuse_gmin = 0, fuse_gmax = -1;
 };
 
 // Split partials of a decode: the workspace's, or a caller-provided buffer of the same shape.
@@ -831,6 +833,8 @@ hw_status launch_decode_merge(hw_ctx *ctx, int32_t layer, int32_t n_new, const f
   a.fuse_blocks = t.fuse_blocks;
   a.fuse_overflow = t.fuse_overflow;
   a.fuse_n_blocks = t.fuse_n_blocks;
+  a.fuse_gmin = t.fuse_gmin;
+  a.fuse_gmax = t.fuse_gmax;
   if (t.bounds) std::copy(t.bounds, t.bounds + t.splits + 1, a.split_begin);
   const int32_t row_blocks = row_blocks_for(ctx, rows, n_new);
   const bool prof = ctx->prof_count < ctx->prof_capacity;
@@ -893,6 +897,8 @@ hw_status decode_planned(hw_ctx *ctx, int32_t layer, int32_t n_new, const float 
     t.fuse_blocks = reinterpret_cast<const int32_t *>(base + ctx->plan_fuse);
     t.fuse_overflow = reinterpret_cast<int32_t *>(base + ctx->plan_cnt) + ctx->cfg.n_layers;
     t.fuse_n_blocks = (int32_t)p.blocks.size();
+    t.fuse_gmin = p.fuse_gmin;
+    t.fuse_gmax = p.fuse_gmax;
   }
   hw_status st = launch_decode_merge(ctx, layer, n_new, q, out, lse, s, t, part);
   if (st == HW_OK) ctx->plan.pending[layer] = 0;
@@ -1282,11 +1288,18 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   // its group 0 (-1: in no view)}.
   std::vector<int32_t> ftab;
   bool fusable = row_blocks_for(ctx, rows_q) == 1;
+  int32_t fgmin = 0, fgmax = -1;
   for (int32_t i = 0; i < n_blocks; ++i) {
     const hw::PlanBlock &pb = ablk[i];
     const int32_t g0 = first_group[block_ids[i]];
     ftab.insert(ftab.end(), {pb.base, pb.tps, pb.row0, g0});
     if (pb.tps > 0 && g0 < 0) fusable = false;
+    if (pb.tps > 0 && g0 >= 0) {
+      const int32_t ga = g0 + pb.base / hw::kTokGroup;
+      const int32_t gz = g0 + (int32_t)(((int64_t)pb.base + (int64_t)n_steps * pb.tps - 1) / hw::kTokGroup);
+      fgmin = fgmax < fgmin ? ga : std::min(fgmin, ga);
+      fgmax = std::max(fgmax, gz);
+    }
   }
   // One upload of the whole region, counters zeroed; the plan is set-up, not a step, so the
   // call waits for it.
@@ -1327,6 +1340,8 @@ hw_status hw_plan_steps(hw_ctx *ctx, int32_t n_steps, int32_t n_blocks, const in
   p.append_blocks = std::move(ablk);
   p.append_pages = std::move(apages);
   p.fusable = fusable;
+  p.fuse_gmin = fgmin;
+  p.fuse_gmax = fgmax;
   p.pending.assign((size_t)g.n_layers, 0);
   ctx->uploaded_valid = false;
   return HW_OK;

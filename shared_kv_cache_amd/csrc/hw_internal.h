@@ -105,6 +105,7 @@ struct DecodeArgs {
   const int32_t *fuse_blocks;
   int32_t *fuse_overflow;
   int32_t fuse_n_blocks;
+  int32_t fuse_gmin, fuse_gmax;   // list indices of the first and last group the window appends to
   // Partition p takes groups [split_begin[p], split_begin[p + 1]) when n_splits <=
   // kMaxBoundSplits (host-chosen, cost-balanced bounds); else [p * n_groups / n_splits, ...).
   int32_t split_begin[kMaxBoundSplits + 1];

@@ -833,9 +833,15 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     pstep = c < a.plan_n_steps ? c : a.plan_n_steps;
   }
   int s_lo = 0, s_hi = -1;
-  if (COOP && end > begin) {
-    s_lo = load_desc<MT>(hd.groups, begin, hd.desc_stride).y >> 8;
-    s_hi = load_desc<MT>(hd.groups, end - 1, hd.desc_stride).y >> 8;   // (segments: no plan term)
+  if constexpr (COOP) {
+    // both ends' descriptors loaded unconditionally (indices clamped), one round trip
+    const int lastg = n_groups > 0 ? n_groups - 1 : 0;
+    const int y0 = load_desc<MT>(hd.groups, min(begin, lastg), hd.desc_stride).y;
+    const int y1 = load_desc<MT>(hd.groups, max(min(end - 1, lastg), 0), hd.desc_stride).y;   // (segments: no plan term)
+    if (end > begin) {
+      s_lo = y0 >> 8;
+      s_hi = y1 >> 8;
+    }
   }
   const int nph = COOP ? (s_hi - s_lo + CAP) / CAP : 1;   // COOP phases (0 without groups)
   GDesc desc, next, next2;
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(NW * 64, 1) void concurrent_decode_kernel(DecodeArg
     if (a.fuse_k != nullptr) {
       if (pcount >= a.plan_n_steps) {   // past the window: nothing is written, the host reports it
         if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) a.fuse_overflow[0] = 1;
-      } else if (wcount > 0) {
+      } else if (wcount > 0 && wfirst <= a.fuse_gmax && wlast >= a.fuse_gmin) {
         bool wrote = false;
         KV *const kw = const_cast<KV *>(kl), *const vw = const_cast<KV *>(vl);
         for (int bi = 0; bi < a.fuse_n_blocks; ++bi) {
