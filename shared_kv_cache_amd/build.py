@@ -26,6 +26,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 arithmetic off on the device: plain scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments preloaded into scalar registers at dispatch (gfx950):
+    # the merge kernel's; kernels whose first argument is a struct preload nothing
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
     "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(PKG, "csrc"),
     "-Wl,-rpath,/opt/rocm/lib",
