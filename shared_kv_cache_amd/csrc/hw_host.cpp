@@ -397,12 +397,18 @@ int32_t auto_splits(const hw_ctx *c, int32_t n_groups, int32_t rows, int32_t n_n
   // w8_32k 19% faster with 4 (256) than with 3; one more partition each spills past one
   // workgroup per CU and is slower. The cooperative (4-wave) kernels also fill every CU:
   // w8_32k's fused step takes 0.3295 ms with 32 partitions, 0.3312 with 24, 0.3338 with 28.
-  const bool coop = hw::decode_waves(c->cfg.kv_dtype, rows, n_new) == 4;
+  const int32_t waves = hw::decode_waves(c->cfg.kv_dtype, rows, n_new);
+  const bool coop = waves == 4;
   const int32_t target = (n_new > 1 || coop) ? c->num_cus : 3 * c->num_cus / 4;
   int32_t s = std::max(1, target / per_head);
-  // At least 4 groups a partition. Small caches still want the parallelism: on w2_4k (142
-  // groups a head) 24 partitions beat 17 (at least 8 groups each) by 2% per step, and 12 by 6%.
+  // At least 4 groups a partition.
   s = std::min(s, std::max(1, n_groups / 4));
+  // Small caches (one token per worker, 8-wave kernels): when a head's groups fit one group
+  // per wave in fewer workgroups than that, the fewest such workgroups. Every wave then makes
+  // one round trip, and fewer workgroups start and write partials. Measured on MI355X, w2_4k
+  // (142 groups a head, replayed steps): 18 partitions (at most 8 groups each) 0.3178 ms per
+  // step, 17 (some waves take two groups) 0.339, 19: 0.3197, 20: 0.3196, 24: 0.3253.
+  if (!coop && n_new == 1) s = std::min(s, std::max(1, (n_groups + waves - 1) / waves));
   // A head of at most 16 groups is two groups for each wave of one workgroup: one partition
   // writes the output directly, with no merge launch (tiny_fp32: 9.3 us a step, 9.8 with two).
   if (n_groups <= 16) s = 1;
