@@ -278,9 +278,9 @@ def describe(r, args, layout):
     """Config and roofline objects of one run_gpu result."""
     wl = r["wl"]
     step_gbps = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
-    default_cfg = (args.query_tokens == 1 and layout == "combined" and not args.splits
-                   and not args.layers)
-    traffic = read_traffic(wl.name) if default_cfg else None
+    default_cfg = layout == "combined" and not args.splits and not args.layers
+    profile_name = wl.name if args.query_tokens == 1 else f"{wl.name}_qt{args.query_tokens}"
+    traffic = read_traffic(profile_name) if default_cfg else None
     config = {
         "workload": wl.name, "layout": layout, "workers": wl.n_workers, "q_heads": wl.n_q_heads,
         "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "layers": wl.n_layers,
