@@ -28,7 +28,7 @@ Sources (pages' titles, section on the page):
 * [P5] kwkr.cn essay on KV-cache sharing vs isolation, s3.2 (KV-cache size
   formula), s6.1 (worked size table).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 rotate-half RoPE pairing (j, j + d/2); frequencies theta^(-2j/d) in fp64;
 softmax scale 1/sqrt(d); GQA mapping kv_head = h // (Hq / Hkv); default
 offsets = running sum of block lengths in view order; default query position =
