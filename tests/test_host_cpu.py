@@ -384,6 +384,22 @@ def test_split_choice_and_override(ctx):
     assert H.hw_debug_resolve(ctx, 0, 1)["n_splits"] == auto
 
 
+@pytest.mark.parametrize("tokens", [16 * 32, 17 * 32, 30 * 32, 100 * 32, 142 * 32 - 5, 190 * 32])
+def test_auto_split_count_rules(tokens):
+    # Without a GPU the library assumes 256 CUs: 3/4 of them over 2 KV heads is 96 partitions,
+    # at least 4 groups each; one partition for at most 16 groups; and a small cache takes the
+    # fewest workgroups whose 8 waves get at most one group each.
+    c = H.hw_create(make_cfg(n_pages=96, max_position=8192))
+    try:
+        _fill(c, 0, {0: tokens})
+        H.hw_set_views(c, [[0]])
+        g = (tokens + 31) // 32
+        want = 1 if g <= 16 else min(96, max(1, g // 4), (g + 7) // 8)
+        assert H.hw_debug_resolve(c, 0, 1)["n_splits"] == want
+    finally:
+        H.hw_destroy(c)
+
+
 @pytest.mark.parametrize("src,nbytes,sink,n_blocks", [
     (0, 1 << 20, 4096, 4),          # no source
     (4096, 1 << 20, 0, 4),          # no sink
